@@ -1,0 +1,193 @@
+"""Python binding of libpuro.so: blockwise-FP8 quantizers and the
+blockwise-scaled FP8 GEMM for MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/puro.h``; PyTorch is used for
+device memory and streams.  There is no fallback: if the library is missing,
+importing this package fails.
+
+The raw C calls keep their C names (``puro_quant_act_1x128``,
+``puro_quant_w_128x128``, ``puro_quant_transpose``,
+``puro_gemm_fp8_blockwise``, ...) and take integer device pointers.  The
+tensor-level helpers ``quant_act_1x128``, ``quant_w_128x128``,
+``quant_transpose``, ``gemm_fp8_blockwise`` allocate outputs with torch and
+call them on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpuro.so")
+
+PURO_OK = 0
+STATUS_NAMES = {0: "PURO_OK", 1: "PURO_ERR_NULL", 2: "PURO_ERR_SHAPE", 3: "PURO_ERR_ALIGN",
+                4: "PURO_ERR_MODE", 5: "PURO_ERR_DTYPE", 6: "PURO_ERR_WORKSPACE",
+                7: "PURO_ERR_DEVICE", 8: "PURO_ERR_LAUNCH", 9: "PURO_ERR_ALIAS"}
+FPROP, DGRAD, WGRAD = 0, 1, 2
+OUT_F32, OUT_BF16 = 0, 1
+T_ACT, T_WEIGHT = 0, 1
+TILE = 128
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libpuro.so is not built: run `python -m blockwise_fp8_gemm_act_amd.build` "
+                      "(or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_lib.puro_quant_act_1x128.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.puro_quant_act_1x128.restype = ctypes.c_int
+_lib.puro_quant_w_128x128.argtypes = [_P, _I64, _I64, _P, _P, _P]
+_lib.puro_quant_w_128x128.restype = ctypes.c_int
+_lib.puro_quant_transpose.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P]
+_lib.puro_quant_transpose.restype = ctypes.c_int
+_lib.puro_gemm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64]
+_lib.puro_gemm_workspace_bytes.restype = ctypes.c_size_t
+_lib.puro_gemm_fp8_blockwise.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
+                                         _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
+_lib.puro_gemm_fp8_blockwise.restype = ctypes.c_int
+_lib.puro_status_str.argtypes = [ctypes.c_int]
+_lib.puro_status_str.restype = ctypes.c_char_p
+_lib.puro_abi_version.argtypes = []
+_lib.puro_abi_version.restype = ctypes.c_int
+
+
+class PuroError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (call, STATUS_NAMES.get(status, status),
+                                                 puro_status_str(status)))
+
+
+# ---------------------------------------------------------------- raw C calls
+def puro_quant_act_1x128(x, rows, cols, q, s, stream=None) -> int:
+    return _lib.puro_quant_act_1x128(x, rows, cols, q, s, stream)
+
+
+def puro_quant_w_128x128(w, rows, cols, q, s, stream=None) -> int:
+    return _lib.puro_quant_w_128x128(w, rows, cols, q, s, stream)
+
+
+def puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream=None) -> int:
+    return _lib.puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream)
+
+
+def puro_gemm_workspace_bytes(mode, M, N, K) -> int:
+    return int(_lib.puro_gemm_workspace_bytes(mode, M, N, K))
+
+
+def puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspace, workspace_bytes,
+                            stream=None) -> int:
+    return _lib.puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspace,
+                                        workspace_bytes, stream)
+
+
+def puro_status_str(status: int) -> str:
+    return _lib.puro_status_str(status).decode()
+
+
+def puro_abi_version() -> int:
+    return int(_lib.puro_abi_version())
+
+
+# ---------------------------------------------------------------- tensor helpers
+def _cdiv(a: int, b: int) -> int:
+    return (a + b - 1) // b
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, call: str):
+    if status != PURO_OK:
+        raise PuroError(status, call)
+
+
+def _bf16_input(x: torch.Tensor, name: str):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise TypeError("%s must be a 2-D bfloat16 CUDA tensor" % name)
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def quant_act_1x128(x: torch.Tensor, q=None, s=None, stream=None):
+    """1x128 tiles: returns (q uint8 [R][C], s fp32 [ceil(C/128)][R])."""
+    _bf16_input(x, "x")
+    R, C = x.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device) if s is None else s
+    _check(puro_quant_act_1x128(x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
+           "puro_quant_act_1x128")
+    return q, s
+
+
+def quant_w_128x128(w: torch.Tensor, q=None, s=None, stream=None):
+    """128x128 blocks: returns (q uint8 [R][C], s fp32 [ceil(R/128)][ceil(C/128)])."""
+    _bf16_input(w, "w")
+    R, C = w.shape
+    q = torch.empty((R, C), dtype=torch.uint8, device=w.device) if q is None else q
+    s = torch.empty((_cdiv(R, TILE), _cdiv(C, TILE)), dtype=torch.float32, device=w.device) if s is None else s
+    _check(puro_quant_w_128x128(w.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
+           "puro_quant_w_128x128")
+    return q, s
+
+
+def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None):
+    """Transposed quantization.  Returns (qt, st) or (qt, st, q_row, s_row) when dual.
+
+    kind T_ACT:    qt [C][R], st [ceil(R/128)][C]; row outputs as quant_act_1x128
+    kind T_WEIGHT: qt [C][R], st [ceil(C/128)][ceil(R/128)]; row outputs as quant_w_128x128
+    """
+    _bf16_input(x, "x")
+    R, C = x.shape
+    dev = x.device
+    qt = torch.empty((C, R), dtype=torch.uint8, device=dev)
+    if kind == T_ACT:
+        st = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
+        s_shape = (_cdiv(C, TILE), R)
+    else:
+        st = torch.empty((_cdiv(C, TILE), _cdiv(R, TILE)), dtype=torch.float32, device=dev)
+        s_shape = (_cdiv(R, TILE), _cdiv(C, TILE))
+    q = s = None
+    if dual:
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s = torch.empty(s_shape, dtype=torch.float32, device=dev)
+    _check(puro_quant_transpose(kind, x.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
+                                q.data_ptr() if dual else None, s.data_ptr() if dual else None,
+                                _stream(stream)), "puro_quant_transpose")
+    return (qt, st, q, s) if dual else (qt, st)
+
+
+def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):
+    n = puro_gemm_workspace_bytes(mode, M, N, K)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device), n
+
+
+def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=None, workspace=None,
+                       stream=None):
+    """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    need = puro_gemm_workspace_bytes(mode, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(puro_gemm_fp8_blockwise(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                                   out.data_ptr(), od, M, N, K, wptr, wbytes, _stream(stream)),
+           "puro_gemm_fp8_blockwise")
+    return out

@@ -1,0 +1,203 @@
+// C ABI of the blockwise-FP8 library: argument validation on the host,
+// device check, dispatch to the gfx950 kernels.  See include/puro.h for the
+// contract of every call.
+//
+// Validation runs entirely on the host and before any HIP call, in this
+// order: mode/kind/dtype, shapes, NULL pointers, alignment, overlaps,
+// workspace; then the device is checked (gfx950) and the kernels are
+// enqueued.  Nothing is enqueued when any check fails.
+#include "puro.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int64_t kMaxGemmK = int64_t(1) << 23;    // 256 rows x K must index in 32 bits
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range rng(const void *p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Any output overlapping any input or another output.
+bool any_alias(const Range *in, int nin, const Range *out, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(out[i], in[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(out[i], out[j])) return true;
+  }
+  return false;
+}
+
+bool shape_ok(int64_t r, int64_t c) {
+  if (r < 0 || c < 0 || r > kMaxDim || c > kMaxDim) return false;
+  if (r > 0 && c > kMaxElems / r) return false;
+  return true;
+}
+
+// Per-device cache of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_dev_ok[64];
+
+puro_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return PURO_ERR_DEVICE;
+  }
+  if (dev < 64) {
+    const int c = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (c == 1) return PURO_OK;
+    if (c == 2) return PURO_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PURO_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? PURO_OK : PURO_ERR_DEVICE;
+}
+
+puro_status launched(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return PURO_ERR_LAUNCH;
+  }
+  return PURO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int puro_abi_version(void) { return PURO_ABI_VERSION; }
+
+const char *puro_status_str(puro_status s) {
+  switch (s) {
+    case PURO_OK: return "ok";
+    case PURO_ERR_NULL: return "a required pointer is NULL";
+    case PURO_ERR_SHAPE: return "invalid shape (negative, not a multiple of 16 where required, or over the limits)";
+    case PURO_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case PURO_ERR_MODE: return "unknown GEMM mode or transpose kind";
+    case PURO_ERR_DTYPE: return "unknown output dtype";
+    case PURO_ERR_WORKSPACE: return "workspace missing or too small";
+    case PURO_ERR_DEVICE: return "no current device, or the device is not gfx950";
+    case PURO_ERR_LAUNCH: return "the HIP runtime failed to enqueue a kernel";
+    case PURO_ERR_ALIAS: return "an output overlaps an input or another output";
+  }
+  return "unknown status";
+}
+
+puro_status puro_quant_act_1x128(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                                 puro_stream_t stream) {
+  if (!shape_ok(rows, cols) || cols % 16 != 0) return PURO_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return PURO_OK;
+  if (!x || !q || !s) return PURO_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return PURO_ERR_ALIGN;
+  const Range in[] = {rng(x, rows * cols * 2)};
+  const Range out[] = {rng(q, rows * cols), rng(s, cdiv(cols, 128) * rows * 4)};
+  if (any_alias(in, 1, out, 2)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_quant_act_1x128(x, rows, cols, q, s, (hipStream_t)stream));
+}
+
+puro_status puro_quant_w_128x128(const uint16_t *w, int64_t rows, int64_t cols, uint8_t *q, float *s,
+                                 puro_stream_t stream) {
+  if (!shape_ok(rows, cols) || cols % 16 != 0) return PURO_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return PURO_OK;
+  if (!w || !q || !s) return PURO_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(s)) return PURO_ERR_ALIGN;
+  const Range in[] = {rng(w, rows * cols * 2)};
+  const Range out[] = {rng(q, rows * cols), rng(s, cdiv(rows, 128) * cdiv(cols, 128) * 4)};
+  if (any_alias(in, 1, out, 2)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_quant_w_128x128(w, rows, cols, q, s, (hipStream_t)stream));
+}
+
+puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *qt, float *st, uint8_t *q_row, float *s_row,
+                                 puro_stream_t stream) {
+  if (kind != PURO_T_ACT && kind != PURO_T_WEIGHT) return PURO_ERR_MODE;
+  if (!shape_ok(rows, cols) || cols % 16 != 0 || rows % 16 != 0) return PURO_ERR_SHAPE;
+  if ((q_row == nullptr) != (s_row == nullptr)) return PURO_ERR_NULL;
+  if (rows == 0 || cols == 0) return PURO_OK;
+  if (!x || !qt || !st) return PURO_ERR_NULL;
+  const bool dual = q_row != nullptr;
+  if (!aligned16(x) || !aligned16(qt) || !aligned16(st)) return PURO_ERR_ALIGN;
+  if (dual && (!aligned16(q_row) || !aligned16(s_row))) return PURO_ERR_ALIGN;
+  const int64_t ni = cdiv(rows, 128), nj = cdiv(cols, 128);
+  const int64_t st_elems = kind == PURO_T_ACT ? ni * cols : nj * ni;
+  const int64_t s_elems = kind == PURO_T_ACT ? nj * rows : ni * nj;
+  const Range in[] = {rng(x, rows * cols * 2)};
+  const Range out[] = {rng(qt, rows * cols), rng(st, st_elems * 4),
+                       rng(q_row, dual ? rows * cols : 0), rng(s_row, dual ? s_elems * 4 : 0)};
+  if (any_alias(in, 1, out, 4)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  if (kind == PURO_T_ACT)
+    return launched(puro::run_quant_t_act(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
+  return launched(puro::run_quant_t_w(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
+}
+
+size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int64_t K) {
+  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return 0;
+  return puro::plan_gemm((int)mode, M, N, K).ws_bytes;
+}
+
+puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const float *sa,
+                                    const uint8_t *b, const float *sb, void *out,
+                                    puro_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                    void *workspace, size_t workspace_bytes, puro_stream_t stream) {
+  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return PURO_ERR_MODE;
+  if (out_dtype != PURO_OUT_F32 && out_dtype != PURO_OUT_BF16) return PURO_ERR_DTYPE;
+  if (!shape_ok(M, K) || !shape_ok(N, K) || !shape_ok(M, N) || K % 16 != 0 || K > kMaxGemmK)
+    return PURO_ERR_SHAPE;
+  if (M == 0 || N == 0) return PURO_OK;
+  if (!out) return PURO_ERR_NULL;
+  const int64_t osz = out_dtype == PURO_OUT_F32 ? 4 : 2;
+  puro::GemmPlan plan{};
+  if (K > 0) {
+    plan = puro::plan_gemm((int)mode, M, N, K);
+    if ((int64_t)plan.tiles_m * plan.tiles_n * plan.splits > kMaxDim) return PURO_ERR_SHAPE;
+    if (!a || !sa || !b || !sb) return PURO_ERR_NULL;
+    if (plan.ws_bytes > 0 && !workspace) return PURO_ERR_WORKSPACE;
+  }
+  if (!aligned16(out)) return PURO_ERR_ALIGN;
+  if (K > 0) {
+    if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb)) return PURO_ERR_ALIGN;
+    if (plan.ws_bytes > 0 && !aligned16(workspace)) return PURO_ERR_ALIGN;
+    const int64_t nk = cdiv(K, 128);
+    const int64_t sb_elems = mode == PURO_WGRAD ? nk * N : cdiv(N, 128) * nk;
+    const Range in[] = {rng(a, M * K), rng(sa, nk * M * 4), rng(b, N * K), rng(sb, sb_elems * 4)};
+    const Range outs[] = {rng(out, M * N * osz), rng(workspace, (int64_t)plan.ws_bytes)};
+    if (any_alias(in, 4, outs, 2)) return PURO_ERR_ALIAS;
+    if (plan.ws_bytes > 0 && workspace_bytes < plan.ws_bytes) return PURO_ERR_WORKSPACE;
+  }
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_gemm((int)mode, a, sa, b, sb, out, out_dtype == PURO_OUT_BF16, M, N, K,
+                                 workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device helpers shared by the gfx950 kernels: bf16 unpacking, the e4m3 tile
+// scale and code rule, DPP reductions.
+//
+// Quantization rule (the pages name DeepSeek-V3's fine-grained block
+// quantization for the main linear layers -- en.roboind.com article on
+// Puro-2B, section "FP8 takes advantage of the RTX 5090's low precision
+// efficiency"; the rule itself is this library's reading):
+//   s = fp32(amax / 448), or 1 when amax == 0
+//   q = e4m3_rne_saturating(fp32(x / s))
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace puro {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 128;          // tile edge (elements)
+constexpr float kE4m3Max = 448.0f;  // largest finite OCP E4M3FN value
+
+// Tiles whose scale is at least this take the reciprocal path for x / s; the
+// rest divide.  For every pair of bf16 values (x, amax) with |x| <= amax and
+// amax >= 2^-104, the reciprocal path yields the same fp32 quotient as an
+// IEEE division whenever |x / s| >= 2^-12, and a value of the same sign below
+// 2^-10 otherwise -- hence the same e4m3 code (checked exhaustively over all
+// such pairs).  s >= 2^-73 implies amax > 2^-65, a wide margin.
+constexpr float kFastDivMinScale = 0x1p-73f;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Scale of a tile from its absolute maximum (IEEE division, no fast-math).
+__device__ __forceinline__ float tile_scale(float amax) {
+  return amax == 0.0f ? 1.0f : amax / kE4m3Max;
+}
+
+// Per-tile constants for quantizing: the scale, its correctly rounded
+// reciprocal, and whether the reciprocal path is valid for this tile.
+struct TileQ {
+  float s;
+  float r;
+  bool fast;
+};
+
+__device__ __forceinline__ TileQ make_tileq(float amax) {
+  TileQ t;
+  t.s = tile_scale(amax);
+  t.r = 1.0f / t.s;
+  t.fast = t.s >= kFastDivMinScale;
+  return t;
+}
+
+// fp32(x / s), exactly, via the reciprocal: y = x*r is within a few ulp of
+// the quotient; one residual step (Markstein) rounds it correctly.  The sign
+// is restored explicitly so that -0 stays -0.
+__device__ __forceinline__ float quot_fast(float x, float s, float r) {
+  float y = x * r;
+  float e = __builtin_fmaf(-y, s, x);
+  float z = __builtin_fmaf(e, r, y);
+  return __builtin_copysignf(z, x);
+}
+
+__device__ __forceinline__ float quot(float x, const TileQ &t) {
+  return t.fast ? quot_fast(x, t.s, t.r) : x / t.s;
+}
+
+// Four fp32 values (already divided by the scale, |v| <= 448 up to one ulp)
+// to four e4m3 codes packed little-endian in one dword.  The hardware
+// conversion rounds to nearest even (OCP E4M3FN on gfx950).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Max over the 16 lanes of a DPP row (lanes 16k .. 16k+15); every lane of the
+// row gets the result.
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
+  return v;
+}
+
+// Max over a whole wave of 64 lanes, returned uniformly.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace puro

@@ -1,0 +1,398 @@
+// Blockwise-scaled FP8 GEMM for gfx950 (CDNA4 matrix cores).
+//
+//   out[m][n] = sum over 128-deep K slices kb of  sA(m,kb) * sB(n,kb) * P_kb[m][n],
+//   P_kb[m][n] = sum_{k in slice kb} dec(a[m][k]) * dec(b[n][k])   (fp32, matrix cores)
+//
+// The pages put the matrix multiplications of the main linear layers on this
+// FP8 path with fine-grained block scaling after DeepSeek-V3 (en.roboind.com
+// article on Puro-2B, section "FP8 takes advantage of the RTX 5090's low
+// precision efficiency").  Both operands are stored K-contiguous ("TN"), so
+// fprop (X W^T), dgrad (dY W, with W's codes pre-transposed) and wgrad
+// (dY^T X, with 128x1-quantized transposes) are all this one contraction; they
+// differ only in B's scale layout:
+//   block-scaled B (fprop, dgrad): sB(n,kb) = sb[n/128][kb]
+//   row-scaled B   (wgrad):        sB(n,kb) = sb[kb][n]
+//
+// Design (MFMA-bound; ~1300-2750 flop per byte of operands at the layer
+// shapes):
+//  - one workgroup of 8 waves computes a 256x256 output tile; each wave owns
+//    64 (M) x 128 (N): 4 x 8 blocks of 16x16, 128 fp32 accumulators per lane;
+//  - each 128-deep K slice of A and B (2 x 32 KB of e4m3) is copied global ->
+//    LDS by the DMA path (global_load_lds_dwordx4, no VGPR round trip) into
+//    one of two buffers while the other is consumed: 128 KB of the 160 KB LDS;
+//  - one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 16x16 block of one
+//    slice, so its result is the slice partial P_kb; it is promoted at once:
+//    acc = fma(P, sA*sB, acc);
+//  - LDS rows are 128 B; the 16-byte chunk c of row r sits at chunk
+//    c ^ ((r & 7) ^ ((r >> 3) & 1)), which makes the fragment reads (16 lanes
+//    reading one chunk column of 16 consecutive rows) bank-conflict free;
+//  - rows past M or N are read from clamped (valid) rows and never stored;
+//    K chunks past K read a 16-byte zero page, so a ragged last slice adds 0;
+//  - optional split-K writes fp32 partials to a workspace that a second
+//    kernel sums in a fixed order (deterministic).
+#include "device_common.h"
+#include "launch.h"
+
+namespace puro {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kThreads = 512;
+constexpr int kSliceBytes = kBM * kBK;            // 32 KB per operand per slice
+
+__device__ __align__(16) uint8_t g_zero16[16];     // zero-initialized at load
+
+struct GemmArgs {
+  const uint8_t *a;
+  const float *sa;
+  const uint8_t *b;
+  const float *sb;
+  void *out;
+  float *ws;
+  int64_t M, N, K;
+  int nk;          // ceil(K / 128)
+  int tiles_m, tiles_n;
+  int splits;      // K-loop splits (1: no workspace)
+  int spl;         // slices per split
+};
+
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Global -> LDS DMA (gfx950 global_load_lds).  The LDS destination of lane i
+// is M0 + 16*i (dwordx4) or M0 + 4*i (dword); M0 is set and restored inside
+// the statement.  These write only LDS (no VGPR results); completion is
+// awaited explicitly with s_waitcnt vmcnt(0) before the barrier that
+// publishes a slice.  They are written as asm so that the compiler does not
+// make every later LDS read wait for them.
+__device__ __forceinline__ void dma16_s(const void *sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void dma16_v(const void *vaddr, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(vaddr), "s"(lds)
+      : "memory");
+}
+__device__ __forceinline__ void dma4_s(const void *sbase, uint32_t voff, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <bool kRowScaledB, bool kBf16Out, bool kToWs>
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
+  // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
+  __shared__ __align__(1024) uint8_t smem[2][2][kSliceBytes];
+  __shared__ __align__(16) float sscale[2][2][kBM];
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = w >> 1, wn = w & 1;
+
+  const int total_tiles = g.tiles_m * g.tiles_n;
+  const int bid = blockIdx.x;
+  const int split = bid / total_tiles;
+  const int tile = bid - split * total_tiles;
+  const int tm = tile % g.tiles_m;       // consecutive workgroups walk down M: they share B
+  const int tn = tile / g.tiles_m;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+  const int kb_begin = split * g.spl;
+  const int kb_end = min(g.nk, kb_begin + g.spl);
+  const int K = (int)g.K;
+
+  // ---- global -> LDS copy plan.  Wave w fills LDS row groups grp = 4w + j
+  // (j = 0..3) of 8 rows; lane -> row grp*8 + (lane/8), physical chunk lane%8,
+  // whose logical chunk is (lane%8) ^ (lane/8) ^ (j&1).  Rows past M / N are
+  // redirected to the tile's first row (finite codes whose products are
+  // never stored).
+  const int rig = lane >> 3;
+  const int kc0 = ((lane & 7) ^ rig) * 16;     // even j
+  const int kc1 = kc0 ^ 16;                     // odd j
+  const uint8_t *a_tile = g.a + m0 * g.K;
+  const uint8_t *b_tile = g.b + n0 * g.K;
+  const int rows_a = (int)min<int64_t>(g.M - m0, kBM);   // valid rows in this tile
+  const int rows_b = (int)min<int64_t>(g.N - n0, kBN);
+  const uint32_t lds0 = lds_addr(&smem[0][0][0]);
+  const uint32_t lds_s0 = lds_addr(&sscale[0][0][0]);
+  const bool ktail = (K & (kBK - 1)) != 0;
+
+  auto issue_slice = [&](int kb, int buf) {
+    const int kofs = kb * kBK;
+    const uint32_t la = lds0 + buf * 2 * kSliceBytes;
+    const uint32_t lb = la + kSliceBytes;
+    if (!(ktail && kb == g.nk - 1)) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int grp = w * 4 + j;
+        const int r = grp * 8 + rig;
+        const int kc = (j & 1) ? kc1 : kc0;
+        const uint32_t offa = (r < rows_a ? r * K : 0) + kc;
+        const uint32_t offb = (r < rows_b ? r * K : 0) + kc;
+        dma16_s(a_tile + kofs, offa, la + grp * 1024);
+        dma16_s(b_tile + kofs, offb, lb + grp * 1024);
+      }
+    } else {
+      // ragged last slice: chunks at or past K read a zero page
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int grp = w * 4 + j;
+        const int r = grp * 8 + rig;
+        const int kc = (j & 1) ? kc1 : kc0;
+        const bool kin = kofs + kc < K;
+        const uint8_t *pa = kin ? a_tile + kofs + (r < rows_a ? r * K : 0) + kc : g_zero16;
+        const uint8_t *pb = kin ? b_tile + kofs + (r < rows_b ? r * K : 0) + kc : g_zero16;
+        dma16_v(pa, la + grp * 1024);
+        dma16_v(pb, lb + grp * 1024);
+      }
+    }
+    // scales: wave 0 copies sA rows m0..m0+255, wave 1 (row-scaled B only) sB columns n0..
+    const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
+    if (w == 0) {
+      const float *src = g.sa + (int64_t)kb * g.M + m0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma4_s(src, (uint32_t)min(lane + 64 * j, rows_a - 1) * 4, ls + 256 * j);
+    }
+    if (kRowScaledB && w == 1) {
+      const float *src = g.sb + (int64_t)kb * g.N + n0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dma4_s(src, (uint32_t)min(lane + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+    }
+  };
+
+  // ---- fragment read plan: lane reads row (lane % 16) of each 16-row block,
+  // logical chunks 2q and 2q+1 (q = lane / 16).
+  const int fr = lane & 15;
+  const int q = lane >> 4;
+  const int p0 = (2 * q) ^ lds_swz(fr);
+  const int p1 = p0 ^ 1;
+  const int64_t nbl = min<int64_t>((n0 + wn * 128) / kBK, (g.N - 1) / kBK);   // block-scaled B row of sb
+  const float *sb_row = g.sb + nbl * g.nk;
+
+  v4f acc[4][8];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  auto load_frag = [&](const uint8_t *base, int r) -> v8i {
+    const uint4 lo = *reinterpret_cast<const uint4 *>(base + r * kBK + p0 * 16);
+    const uint4 hi = *reinterpret_cast<const uint4 *>(base + r * kBK + p1 * 16);
+    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+
+  if (kb_begin < kb_end) issue_slice(kb_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const int buf = (kb - kb_begin) & 1;
+    if (kb + 1 < kb_end) issue_slice(kb + 1, buf ^ 1);
+
+    const uint8_t *As = smem[buf][0];
+    const uint8_t *Bs = smem[buf][1];
+    const float *lsa = sscale[buf][0];
+    const float *lsb = sscale[buf][1];
+
+    v8i af[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[mb] = load_frag(As, wm * 64 + mb * 16 + fr);
+    v4f sa[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) sa[mb] = *reinterpret_cast<const v4f *>(&lsa[wm * 64 + mb * 16 + 4 * q]);
+    if constexpr (!kRowScaledB) {
+      const float sbv = sb_row[kb];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sa[mb] *= sbv;
+    }
+
+    // Pipeline: the MFMAs of n-block nb are issued while the partials of
+    // n-block nb-1 are promoted, so no FMA waits on the MFMA it reads.
+    v4f P[4];
+    v4f sc[4];
+    {
+      const v8i b0 = load_frag(Bs, wn * 128 + fr);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mb], b0, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      if constexpr (kRowScaledB) {
+        const float sbn = lsb[wn * 128 + fr];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) sc[mb] = sa[mb] * sbn;
+      }
+    }
+#pragma unroll
+    for (int nb = 1; nb <= 8; ++nb) {
+      __builtin_amdgcn_sched_barrier(0);
+      v8i bn;
+      float sbn = 1.0f;
+      if (nb < 8) {
+        bn = load_frag(Bs, wn * 128 + nb * 16 + fr);
+        if constexpr (kRowScaledB) sbn = lsb[wn * 128 + nb * 16 + fr];
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if constexpr (kRowScaledB)
+          acc[mb][nb - 1] = __builtin_elementwise_fma(P[mb], sc[mb], acc[mb][nb - 1]);
+        else
+          acc[mb][nb - 1] = __builtin_elementwise_fma(P[mb], sa[mb], acc[mb][nb - 1]);
+        if (nb < 8)
+          P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mb], bn, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+      }
+      if constexpr (kRowScaledB) {
+        if (nb < 8) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) sc[mb] = sa[mb] * sbn;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows m0 + wm*64 + mb*16 + 4q + e, columns n0 + wn*128 + nb*16 + fr
+  const int64_t mrow0 = m0 + wm * 64 + 4 * q;
+  const int64_t ncol0 = n0 + wn * 128 + fr;
+  const bool full = m0 + kBM <= g.M && n0 + kBN <= g.N;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t m = mrow0 + mb * 16 + e;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int64_t n = ncol0 + nb * 16;
+        if (!full && (m >= g.M || n >= g.N)) continue;
+        const float v = acc[mb][nb][e];
+        if constexpr (kToWs) {
+          g.ws[((int64_t)split * g.M + m) * g.N + n] = v;
+        } else if constexpr (kBf16Out) {
+          reinterpret_cast<uint16_t *>(g.out)[m * g.N + n] = (uint16_t)f32_to_bf16_rne(v);
+        } else {
+          reinterpret_cast<float *>(g.out)[m * g.N + n] = v;
+        }
+      }
+    }
+}
+
+// Sum of the split-K partials in increasing split order.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, void *out, int64_t MN, int splits) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+    float v = ws[i];
+    for (int s = 1; s < splits; ++s) v += ws[(int64_t)s * MN + i];
+    if constexpr (kBf16Out)
+      reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float *>(out)[i] = v;
+  }
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void fill_zero_kernel(void *out, int64_t MN) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+    if constexpr (kBf16Out)
+      reinterpret_cast<uint16_t *>(out)[i] = 0;
+    else
+      reinterpret_cast<float *>(out)[i] = 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------- planning
+
+GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{};
+  p.nk = (int)((K + kBK - 1) / kBK);
+  p.tiles_m = (int)((M + kBM - 1) / kBM);
+  p.tiles_n = (int)((N + kBN - 1) / kBN);
+  p.splits = 1;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  // Too few output tiles to occupy the 256 compute units: split the K loop,
+  // keeping at least 8 slices per split.
+  if (tiles > 0 && p.nk > 0) {
+    int s = 1;
+    while (tiles * s < 256 && p.nk / (2 * s) >= 8 && s < 8) s *= 2;
+    p.splits = s;
+  }
+  p.spl = (p.nk + p.splits - 1) / p.splits;
+  if (p.spl > 0) p.splits = (p.nk + p.spl - 1) / p.spl;
+  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+  (void)mode;
+  return p;
+}
+
+hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                    void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, void *ws,
+                    hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const int64_t MN = M * N;
+  if (K == 0) {
+    const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 65536);
+    if (bf16_out) hipLaunchKernelGGL(fill_zero_kernel<true>, dim3(blocks), dim3(256), 0, stream, out, MN);
+    else hipLaunchKernelGGL(fill_zero_kernel<false>, dim3(blocks), dim3(256), 0, stream, out, MN);
+    return hipGetLastError();
+  }
+  const GemmPlan p = plan_gemm(mode, M, N, K);
+  GemmArgs g{};
+  g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.out = out; g.ws = (float *)ws;
+  g.M = M; g.N = N; g.K = K;
+  g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
+  g.splits = p.splits; g.spl = p.spl;
+  const dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n * p.splits));
+  const bool row_b = mode == 2;
+  const bool to_ws = p.splits > 1;
+#define PURO_LAUNCH(RB, BF, WS) \
+  hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, BF, WS>), grid, dim3(kThreads), 0, stream, g)
+  if (to_ws) {
+    if (row_b) PURO_LAUNCH(true, false, true); else PURO_LAUNCH(false, false, true);
+  } else if (bf16_out) {
+    if (row_b) PURO_LAUNCH(true, true, false); else PURO_LAUNCH(false, true, false);
+  } else {
+    if (row_b) PURO_LAUNCH(true, false, false); else PURO_LAUNCH(false, false, false);
+  }
+#undef PURO_LAUNCH
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !to_ws) return err;
+  const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 8192);
+  if (bf16_out)
+    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
+  return hipGetLastError();
+}
+
+}  // namespace puro

@@ -1,0 +1,35 @@
+// Internal launchers behind the C ABI (host side).  Arguments are already
+// validated by the ABI layer when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace puro {
+
+hipError_t run_quant_act_1x128(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, float *s,
+                               hipStream_t stream);
+hipError_t run_quant_w_128x128(const uint16_t *w, int64_t R, int64_t C, uint8_t *q, float *s,
+                               hipStream_t stream);
+hipError_t run_quant_t_act(const uint16_t *x, int64_t R, int64_t C, uint8_t *qt, float *st,
+                           uint8_t *q, float *s, hipStream_t stream);
+hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, float *st,
+                         uint8_t *q, float *s, hipStream_t stream);
+
+struct GemmPlan {
+  int nk;          // 128-deep K slices
+  int tiles_m, tiles_n;
+  int splits;      // K-loop splits
+  int spl;         // slices per split
+  size_t ws_bytes; // fp32 split-K partials
+};
+
+// Deterministic launch plan of a GEMM shape (host only, no device access).
+GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K);
+
+hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                    void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, void *ws,
+                    hipStream_t stream);
+
+}  // namespace puro

@@ -1,0 +1,164 @@
+/*
+ * puro.h -- C ABI of the blockwise-FP8 quantizers and the blockwise-scaled
+ * FP8 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute.  The pages on Puro-2B (en.roboind.com article,
+ * section "FP8 takes advantage of the RTX 5090's low precision efficiency")
+ * put the matrix multiplications of the main linear layers on an FP8 path
+ * that follows DeepSeek-V3's fine-grained block quantization, and keep the
+ * numerically sensitive operations and the training state in BF16/FP32; the
+ * ainews.surl.tw article adds that training uses blockwise FP8 to cut compute
+ * and memory.  The pages give no formulas; this library fixes them as:
+ *
+ *   tile scale   s = amax / 448 (IEEE fp32 division), s = 1 for an all-zero tile
+ *   code         q = e4m3(fp32(x / s)): OCP E4M3FN, round to nearest even,
+ *                saturating at +-448; -0 and negative values that round to zero
+ *                give 0x80
+ *   1x128 tile   128 consecutive elements of one row (activations)
+ *   128x128 tile 128 rows x 128 columns (weights)
+ *   128x1 tile   128 consecutive rows of one column (the transposed wgrad
+ *                operands, quantized from the bf16 original)
+ *   GEMM         out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k], with each
+ *                128-deep slice of k summed in fp32 and added into an fp32
+ *                accumulator after multiplying by the slice's two scales.
+ *
+ * Ragged shapes.  A row length that is not a multiple of 128 leaves a short
+ * last tile that covers only the elements that exist.  Row lengths (the
+ * contraction extent of every code tensor) must be multiples of 16; row
+ * counts are free.  Sizes of 0 are allowed and enqueue nothing (a GEMM with
+ * K = 0 writes zeros).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, and
+ *     16-byte aligned.  bf16 tensors are passed as uint16_t bit patterns.
+ *   - The caller allocates and frees every buffer (the library never allocates
+ *     device memory), keeps them alive until the stream has passed the call,
+ *     and must not let any output overlap any input or another output.
+ *   - Every call validates its arguments on the host first.  On any error it
+ *     enqueues nothing, touches no output and returns the error code.  Launch
+ *     failures return PURO_ERR_LAUNCH.  No exception or abort crosses the ABI.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without waiting for it.
+ *   - Inputs must be finite; non-finite inputs are outside the contract.
+ *   - Calls are thread-safe and keep no per-call state.
+ *   - Limits: every dimension < 2^31 and every tensor < 2^40 elements
+ *     (PURO_ERR_SHAPE otherwise).
+ */
+#ifndef PURO_H
+#define PURO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PURO_ABI_VERSION 1
+
+typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
+
+typedef enum {
+    PURO_OK = 0,
+    PURO_ERR_NULL = 1,        /* a required pointer is NULL */
+    PURO_ERR_SHAPE = 2,       /* negative size, row length not a multiple of 16, or over the limits */
+    PURO_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned */
+    PURO_ERR_MODE = 4,        /* unknown GEMM mode or transpose kind */
+    PURO_ERR_DTYPE = 5,       /* unknown output dtype */
+    PURO_ERR_WORKSPACE = 6,   /* workspace missing or smaller than puro_gemm_workspace_bytes() */
+    PURO_ERR_DEVICE = 7,      /* the current device is not gfx950, or no device */
+    PURO_ERR_LAUNCH = 8,      /* the HIP runtime reported an error while enqueueing */
+    PURO_ERR_ALIAS = 9        /* an output overlaps an input or another output */
+} puro_status;
+
+typedef enum {
+    PURO_FPROP = 0,   /* Y  = X  W^T : a = act codes of X  [T][K_in],      b = weight codes of W [N_out][K_in] */
+    PURO_DGRAD = 1,   /* dX = dY W   : a = act codes of dY [T][N_out],     b = transposed weight codes [K_in][N_out] */
+    PURO_WGRAD = 2    /* dW = dY^T X : a = 128x1 codes of dY [N_out][T],   b = 128x1 codes of X [K_in][T] */
+} puro_gemm_mode;
+
+typedef enum { PURO_OUT_F32 = 0, PURO_OUT_BF16 = 1 } puro_out_dtype;
+
+typedef enum { PURO_T_ACT = 0, PURO_T_WEIGHT = 1 } puro_t_kind;
+
+/*
+ * puro_quant_act_1x128 -- activation quantization, one scale per 1x128 tile.
+ *   x     [rows][cols] bf16 (input)
+ *   q     [rows][cols] uint8 e4m3 codes (output)
+ *   s     [ceil(cols/128)][rows] fp32 (output): s[j][r] is the scale of the
+ *         tile x[r][128j .. min(128j+128, cols)-1]
+ * cols must be a multiple of 16.
+ */
+puro_status puro_quant_act_1x128(const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *q, float *s, puro_stream_t stream);
+
+/*
+ * puro_quant_w_128x128 -- weight quantization, one scale per 128x128 block.
+ *   w     [rows][cols] bf16 (input)
+ *   q     [rows][cols] uint8 codes (output)
+ *   s     [ceil(rows/128)][ceil(cols/128)] fp32 (output), block (i, j) covers
+ *         rows 128i.. and columns 128j.. (short at a ragged edge)
+ * cols must be a multiple of 16.
+ */
+puro_status puro_quant_w_128x128(const uint16_t *w, int64_t rows, int64_t cols,
+                                 uint8_t *q, float *s, puro_stream_t stream);
+
+/*
+ * puro_quant_transpose -- transposed (re)quantization for the backward pass,
+ * from the bf16 original, in one read of x.
+ *   kind == PURO_T_ACT: 128x1 tiles (128 consecutive rows of one column).
+ *     qt [cols][rows] uint8: qt[c][r] is the code of x[r][c]
+ *     st [ceil(rows/128)][cols] fp32: st[i][c] is the scale of x[128i..][c]
+ *     q_row, s_row (optional, both NULL or both set): the same pass also
+ *       writes exactly what puro_quant_act_1x128(x) writes.
+ *   kind == PURO_T_WEIGHT: 128x128 blocks, stored transposed.
+ *     qt [cols][rows] uint8: the transpose of puro_quant_w_128x128's codes
+ *     st [ceil(cols/128)][ceil(rows/128)] fp32: st[j][i] = scale of block (i, j)
+ *     q_row, s_row (optional): exactly what puro_quant_w_128x128(x) writes.
+ * Both rows and cols must be multiples of 16.
+ */
+puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *qt, float *st, uint8_t *q_row, float *s_row,
+                                 puro_stream_t stream);
+
+/*
+ * puro_gemm_workspace_bytes -- device workspace that puro_gemm_fp8_blockwise
+ * needs for this mode and shape (0 when none).  Deterministic: the same
+ * arguments always give the same size and the same split of the K loop.
+ */
+size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int64_t K);
+
+/*
+ * puro_gemm_fp8_blockwise -- blockwise-scaled FP8 GEMM.
+ *   out[m][n] = sum_k (dec(a[m][k]) * sa[k/128][m]) * (dec(b[n][k]) * sb(n, k))
+ *   a    [M][K] uint8 codes,  sa [ceil(K/128)][M] fp32
+ *   b    [N][K] uint8 codes
+ *   sb   FPROP/DGRAD: [ceil(N/128)][ceil(K/128)] fp32, sb(n, k) = sb[n/128][k/128]
+ *        WGRAD:       [ceil(K/128)][N] fp32,            sb(n, k) = sb[k/128][n]
+ *   out  [M][N] fp32 or bf16 (round to nearest even)
+ *   workspace / workspace_bytes: at least puro_gemm_workspace_bytes(mode, M, N, K)
+ *        bytes of device memory (may be NULL when that is 0); its contents on
+ *        entry do not matter.
+ * K must be a multiple of 16; M and N are free.  Each 128-deep slice of K is
+ * accumulated by the matrix cores in fp32 and promoted into the fp32
+ * accumulator with its scales; the result is deterministic for a given shape.
+ */
+puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode,
+                                    const uint8_t *a, const float *sa,
+                                    const uint8_t *b, const float *sb,
+                                    void *out, puro_out_dtype out_dtype,
+                                    int64_t M, int64_t N, int64_t K,
+                                    void *workspace, size_t workspace_bytes,
+                                    puro_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *puro_status_str(puro_status s);
+
+/* PURO_ABI_VERSION of the built library. */
+int puro_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PURO_H */

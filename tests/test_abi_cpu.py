@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/puro.h declares, and rejects invalid arguments on the host before it
+touches a device (fake, never dereferenced pointers are enough for that).
+On a machine without a GPU a valid call stops at the device check."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "puro.h")
+
+import blockwise_fp8_gemm_act_amd as puro  # noqa: E402
+
+OK, NULL, SHAPE, ALIGN, MODE, DTYPE, WS, DEVICE, LAUNCH, ALIAS = range(10)
+
+# fake, 16-byte aligned, well separated device addresses (never dereferenced)
+A0, A1, A2, A3, A4, A5, A6 = (0x7F0000000000 + i * (1 << 32) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(puro_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
+                            "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
+                            "puro_status_str", "puro_abi_version"])
+
+
+def test_library_exports_every_declared_function():
+    out = subprocess.run(["nm", "-D", "--defined-only", puro.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (puro_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert callable(getattr(puro._lib, name))
+
+
+def test_version_and_status_strings():
+    assert puro.puro_abi_version() == 1
+    for s in range(10):
+        assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
+    assert puro.puro_status_str(99) == "unknown status"
+
+
+def no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+# ---------------------------------------------------------------- quantizers
+def test_quant_act_validation():
+    f = puro.puro_quant_act_1x128
+    assert f(A0, -1, 128, A1, A2) == SHAPE
+    assert f(A0, 4, 100, A1, A2) == SHAPE                 # cols not a multiple of 16
+    assert f(A0, 1 << 31, 128, A1, A2) == SHAPE           # over the dimension limit
+    assert f(A0, 1 << 30, 1 << 20, A1, A2) == SHAPE       # over the element limit
+    assert f(None, 0, 128, None, None) == OK              # empty: nothing to do
+    assert f(A0, 4, 0, A1, A2) == OK
+    assert f(None, 4, 128, A1, A2) == NULL
+    assert f(A0, 4, 128, None, A2) == NULL
+    assert f(A0, 4, 128, A1, None) == NULL
+    assert f(A0 + 8, 4, 128, A1, A2) == ALIGN
+    assert f(A0, 4, 128, A1 + 4, A2) == ALIGN
+    assert f(A0, 4, 128, A0 + 512, A2) == ALIAS           # q inside x
+    assert f(A0, 4, 128, A1, A1 + 256) == ALIAS           # s inside q
+    if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
+        assert f(A0, 4, 128, A1, A1 + 512) == DEVICE
+
+
+def test_quant_w_validation():
+    f = puro.puro_quant_w_128x128
+    assert f(A0, 128, 120, A1, A2) == SHAPE
+    assert f(A0, 128, 128, None, A2) == NULL
+    assert f(A0, 128, 128, A1, A2 + 4) == ALIGN
+    assert f(A0, 128, 128, A1, A1) == ALIAS
+
+
+def test_quant_transpose_validation():
+    f = puro.puro_quant_transpose
+    assert f(2, A0, 128, 128, A1, A2, None, None) == MODE
+    assert f(0, A0, 120, 128, A1, A2, None, None) == SHAPE    # rows must be a multiple of 16 here
+    assert f(1, A0, 128, 8, A1, A2, None, None) == SHAPE
+    assert f(0, A0, 128, 128, A1, A2, A3, None) == NULL       # q_row without s_row
+    assert f(0, A0, 128, 128, None, A2, None, None) == NULL
+    assert f(0, A0, 128, 128, A1, A2, A3 + 8, A4) == ALIGN
+    assert f(0, A0, 128, 128, A1, A2, A1 + 1024, A4) == ALIAS  # q_row overlaps qt
+    assert f(0, A0, 0, 128, None, None, None, None) == OK
+
+
+# ---------------------------------------------------------------- GEMM
+def test_gemm_validation():
+    f = puro.puro_gemm_fp8_blockwise
+    M, N, K = 256, 256, 256
+    args = dict(a=A0, sa=A1, b=A2, sb=A3, out=A4)
+
+    def call(mode=0, od=0, M=M, N=N, K=K, ws=None, wsb=0, **kw):
+        a = dict(args, **kw)
+        return f(mode, a["a"], a["sa"], a["b"], a["sb"], a["out"], od, M, N, K, ws, wsb)
+
+    assert call(mode=3) == MODE
+    assert call(mode=-1) == MODE
+    assert call(od=2) == DTYPE
+    assert call(K=100) == SHAPE
+    assert call(M=-5) == SHAPE
+    assert call(K=1 << 24) == SHAPE
+    assert call(M=0) == OK and call(N=0) == OK
+    assert call(out=None) == NULL
+    assert call(a=None) == NULL
+    assert call(sb=None) == NULL
+    assert call(a=A0 + 1) == ALIGN
+    assert call(out=A4 + 2) == ALIGN
+    assert call(out=A0) == ALIAS
+    assert call(out=A3) == ALIAS                          # out starts on sb
+    if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
+        assert call() == DEVICE
+        assert call(K=0, a=None, sa=None, b=None, sb=None) == DEVICE
+
+
+def test_gemm_workspace_sizing():
+    ws = puro.puro_gemm_workspace_bytes
+    # invalid arguments size to 0
+    assert ws(5, 256, 256, 256) == 0 and ws(0, 0, 256, 256) == 0 and ws(0, 256, 256, -1) == 0
+    # plenty of output tiles: no split
+    assert ws(0, 4096, 4096, 2048) == 0
+    # deterministic
+    for shape in [(2, 2048, 6144, 8192), (2, 2048, 2048, 16384), (0, 256, 256, 8192)]:
+        assert ws(*shape) == ws(*shape)
+    # a split-K shape has fp32 partials for every split
+    n = ws(2, 2048, 2048, 16384)
+    assert n > 0 and n % (2048 * 2048 * 4) == 0
+
+
+def test_gemm_workspace_errors():
+    f = puro.puro_gemm_fp8_blockwise
+    M, N, K = 2048, 2048, 16384
+    need = puro.puro_gemm_workspace_bytes(2, M, N, K)
+    assert need > 0
+    assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, None, 0) == WS
+    assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5, need - 16) == WS
+    assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5 + 4, need) == ALIGN
+    assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A4 + 16, need) == ALIAS
+    if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
+        assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5, need) == DEVICE

@@ -1,0 +1,168 @@
+"""GPU parity of the blockwise-scaled FP8 GEMM against the oracle's fp64 GEMM.
+
+Operands are made by the oracle quantizers on the host (so these tests
+isolate the GEMM) except in the end-to-end test, which quantizes on the GPU.
+fp32 outputs: normalized error <= 1e-4; integer-valued cases bit-exact.
+bf16 outputs: within 1 ulp of the oracle's rounding, or normalized error <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import (DGRAD, FPROP, WGRAD, bf16_bits_np, cdiv, check_gemm_values,
+                     quantized_operands, to_np, TILE)
+from workloads import bits, make
+
+pytestmark = pytest.mark.gpu
+
+puro = pytest.importorskip("blockwise_fp8_gemm_act_amd")
+
+
+def run_gpu(mode, a, sa, b, sb, dtype):
+    out = puro.gemm_fp8_blockwise(mode, torch.from_numpy(a).cuda(), torch.from_numpy(sa).cuda(),
+                                  torch.from_numpy(b).cuda(), torch.from_numpy(sb).cuda(), out_dtype=dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def out_np(out):
+    return bf16_bits_np(out) if out.dtype == torch.bfloat16 else to_np(out)
+
+
+def check_full(orc, mode, a, sa, b, sb, dtype, what):
+    out = run_gpu(mode, a, sa, b, sb, dtype)
+    ref = orc.gemm(mode, a, sa, b, sb)
+    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
+    o = out_np(out)
+    ov = o if dtype == torch.float32 else out.float().cpu().numpy()
+    if dtype == torch.bfloat16:
+        return check_gemm_values_bf16(orc, o, ov, ref, na, nb, what)
+    return check_gemm_values(ov, ref, na[:, None], nb[None, :], False, orc, what)
+
+
+def check_gemm_values_bf16(orc, o16, ov, ref, na, nb, what):
+    denom = na[:, None] * nb[None, :]
+    err = np.abs(ov.astype(np.float64) - ref)
+    norm = np.where(denom > 0, err / np.where(denom > 0, denom, 1), np.where(err == 0, 0, np.inf))
+    from helpers import bf16_ordered, GEMM_TOL
+    ref16 = orc.f64_to_bf16_array(ref)
+    ulps = np.abs(bf16_ordered(o16) - bf16_ordered(ref16))
+    ok = (ulps <= 1) | (norm <= GEMM_TOL)
+    assert ok.all(), "%s: %d elements beyond 1 ulp and tolerance" % (what, int((~ok).sum()))
+    assert norm.max() <= GEMM_TOL
+    return float(norm.max()), float(np.mean(ulps <= 1))
+
+
+def test_tiny_fprop_workload_fp32(orc):
+    """256x256 activations (2 outlier channels) x 512x256 weight -> fp32, seed 0."""
+    t = make("tiny_fprop")
+    a, sa = orc.quant_act_1x128(bits(t["x"]))
+    b, sb = orc.quant_w_128x128(bits(t["w"]))
+    worst, _ = check_full(orc, FPROP, a, sa, b, sb, torch.float32, "tiny fprop")
+    assert worst < 1e-6
+
+
+@pytest.mark.parametrize("mode", [FPROP, DGRAD, WGRAD])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 200, 272), (512, 768, 1024)])
+def test_integer_valued_bit_exact(orc, mode, M, N, K):
+    """Codes of the integers -8..8 with power-of-two scales: every partial sum
+    is exact in fp32, so the fp32 output must equal the oracle bit for bit."""
+    rng = np.random.default_rng(M + N + K + mode)
+    codes = np.array([orc.e4m3_encode(float(v)) for v in range(-8, 9)], dtype=np.uint8)
+    nk = cdiv(K, TILE)
+    a = rng.choice(codes, size=(M, K)).astype(np.uint8)
+    b = rng.choice(codes, size=(N, K)).astype(np.uint8)
+    sa = (np.float32(2.0) ** rng.integers(-3, 4, size=(nk, M))).astype(np.float32)
+    sbs = (nk, N) if mode == WGRAD else (cdiv(N, TILE), nk)
+    sb = (np.float32(2.0) ** rng.integers(-3, 4, size=sbs)).astype(np.float32)
+    out = to_np(run_gpu(mode, a, sa, b, sb, torch.float32))
+    ref = orc.gemm(mode, a, sa, b, sb)
+    assert np.array_equal(out.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("mode", [FPROP, DGRAD, WGRAD])
+@pytest.mark.parametrize("M,N,K", [(200, 300, 144), (1, 17, 16), (257, 129, 400), (640, 384, 2048)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ragged_shapes(orc, mode, M, N, K, dtype):
+    a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=M * 7 + N + K)
+    check_full(orc, mode, a, sa, b, sb, dtype, "mode %d %dx%dx%d" % (mode, M, N, K))
+
+
+@pytest.mark.parametrize("mode", [FPROP, WGRAD])
+def test_split_k_path(orc, mode):
+    M, N, K = 512, 512, 4096
+    assert puro.puro_gemm_workspace_bytes(mode, M, N, K) > 0
+    a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=99)
+    for dtype in (torch.float32, torch.bfloat16):
+        check_full(orc, mode, a, sa, b, sb, dtype, "split-K mode %d" % mode)
+
+
+def test_zero_k_writes_zeros():
+    for dtype in (torch.float32, torch.bfloat16):
+        a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
+        b = torch.zeros((7, 0), dtype=torch.uint8, device="cuda")
+        sa = torch.zeros((0, 5), dtype=torch.float32, device="cuda")
+        sb = torch.zeros((1, 0), dtype=torch.float32, device="cuda")
+        out = torch.full((5, 7), 3.0, dtype=dtype, device="cuda")
+        puro.gemm_fp8_blockwise(FPROP, a, sa, b, sb, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0)
+
+
+def sample_positions(M, N, n, seed):
+    rng = np.random.default_rng(seed)
+    ms = np.concatenate([rng.integers(0, M, n), np.full(64, M - 1), np.zeros(64, np.int64)])
+    ns = np.concatenate([rng.integers(0, N, n), rng.integers(0, N, 64), np.arange(64) % N])
+    return ms, ns
+
+
+@pytest.mark.parametrize("which", ["qkv_fprop", "mlp_down_dgrad", "mlp_down_wgrad"])
+def test_workload_sizes_sampled(orc, which):
+    """Full-size GEMMs, in the launch configuration the benchmark uses,
+    checked on 4096 sampled outputs plus the first and last rows."""
+    if which == "qkv_fprop":
+        t = make("qkv_fprop")
+        a, sa = orc.quant_act_1x128(bits(t["x"]))
+        b, sb = orc.quant_w_128x128(bits(t["w"]))
+        mode, dtype = FPROP, torch.bfloat16
+    else:
+        t = make("mlp_down_bwd")
+        if which == "mlp_down_dgrad":
+            a, sa = orc.quant_act_1x128(bits(t["dy"]))
+            b, sb = orc.quant_w_128x128_t(bits(t["w"]))
+            mode, dtype = DGRAD, torch.bfloat16
+        else:
+            a, sa = orc.quant_act_128x1_t(bits(t["dy"]))
+            b, sb = orc.quant_act_128x1_t(bits(t["x"]))
+            mode, dtype = WGRAD, torch.float32
+    M, N = a.shape[0], b.shape[0]
+    out = run_gpu(mode, a, sa, b, sb, dtype)
+    ms, ns = sample_positions(M, N, 4096, {"qkv_fprop": 1, "mlp_down_dgrad": 2, "mlp_down_wgrad": 3}[which])
+    ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
+    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
+    o = out_np(out)
+    if dtype == torch.bfloat16:
+        ov = out.float().cpu().numpy()[ms, ns]
+        from helpers import bf16_ordered, GEMM_TOL
+        ref16 = orc.f64_to_bf16_array(ref)
+        ulps = np.abs(bf16_ordered(o[ms, ns]) - bf16_ordered(ref16))
+        norm = np.abs(ov - ref) / (na[ms] * nb[ns])
+        assert np.all((ulps <= 1) | (norm <= GEMM_TOL))
+        assert norm.max() <= GEMM_TOL
+    else:
+        check_gemm_values(o[ms, ns], ref, na[ms], nb[ns], False, orc, which)
+
+
+def test_end_to_end_gpu_quantizers(orc):
+    """Quantize on the GPU, multiply on the GPU; compare with oracle quantize + oracle GEMM."""
+    t = make("tiny_fprop")
+    x, w = t["x"].cuda(), t["w"].cuda()
+    a, sa = puro.quant_act_1x128(x)
+    b, sb = puro.quant_w_128x128(w)
+    out = puro.gemm_fp8_blockwise(FPROP, a, sa, b, sb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oa, osa = orc.quant_act_1x128(bits(t["x"]))
+    ob, osb = orc.quant_w_128x128(bits(t["w"]))
+    ref = orc.gemm(FPROP, oa, osa, ob, osb)
+    na, nb = orc.deq_row_norms(FPROP, oa, osa, ob, osb)
+    check_gemm_values(to_np(out), ref, na[:, None], nb[None, :], False, orc, "end to end")
