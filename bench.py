@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Benchmark of the blockwise-FP8 path on one MI355X (gfx950).
+
+One step = one pass of the whole path over one Qwen3-1.7B-shaped layer
+(Puro-2B: hidden 2048, 16 query + 8 key/value heads of 128, MLP 6144) at
+16384 tokens: for each of the four main linears (QKV 2048->4096, O
+2048->2048, gate_up 2048->12288, down 6144->2048)
+  - dual 128x1 / 1x128 quantization of the input X (one read of X),
+  - dual transposed / plain 128x128 quantization of the weight W,
+  - dual 128x1 / 1x128 quantization of the output gradient dY,
+  - fprop  Y  = X W^T     (bf16 out),
+  - dgrad  dX = dY W      (bf16 out),
+  - wgrad  dW = dY^T X    (fp32 out, contracting over the tokens).
+Inputs are seeded synthetic tensors (see workloads.py) resident in HBM before
+the timed region.  The reported value is GEMM TFLOP/s over the whole step
+(quantizers included in the time).
+
+Prints ONE JSON line.  Options: --steps K --warmup W (defaults 20 / 5),
+--gpus N (only 1 is supported: the path is measured on one GPU),
+--workload {layer, qkv_fprop, mlp_fprop, mlp_down_bwd}, --no-cpu-baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_FLOPS = 5.0e15      # MI355X dense FP8 MFMA, published
+PEAK_HBM_BPS = 8.0e12        # MI355X HBM3E, published
+METRIC = "blockwise-FP8 GEMM TFLOP/s & % FP8 MFMA peak; quantizer GB/s, Puro-2B shapes"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_fp8_gemm_act_amd", "csrc", f)
+                  for f in ("gemm.hip", "device_common.h")]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer", choices=["layer", "qkv_fprop", "mlp_fprop", "mlp_down_bwd"])
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+class Launch:
+    """One kernel launch of a step: what it is and its algorithmic work."""
+
+    def __init__(self, kind, name, fn, flops=0.0, bytes_=0.0):
+        self.kind, self.name, self.fn, self.flops, self.bytes = kind, name, fn, flops, bytes_
+
+
+def build_plan(workload, tensors, puro, torch):
+    """Allocate every output once and return the list of launches of one step."""
+    dev = "cuda"
+    stream = torch.cuda.current_stream().cuda_stream
+    keep = []
+    launches = []
+
+    def alloc(shape, dtype):
+        t = torch.empty(shape, dtype=dtype, device=dev)
+        keep.append(t)
+        return t
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (what, puro.puro_status_str(st)))
+
+    def q_act_dual(x, name):
+        R, C = x.shape
+        qt, st = alloc((C, R), torch.uint8), alloc((cdiv(R, 128), C), torch.float32)
+        q, s = alloc((R, C), torch.uint8), alloc((cdiv(C, 128), R), torch.float32)
+        args = (puro.T_ACT, x.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(), q.data_ptr(), s.data_ptr(), stream)
+        launches.append(Launch("quant", name, lambda: check(puro.puro_quant_transpose(*args), name),
+                               bytes_=R * C * (2 + 2 * (1 + 4 / 128))))
+        return (q, s), (qt, st)
+
+    def q_act(x, name):
+        R, C = x.shape
+        q, s = alloc((R, C), torch.uint8), alloc((cdiv(C, 128), R), torch.float32)
+        args = (x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), stream)
+        launches.append(Launch("quant", name, lambda: check(puro.puro_quant_act_1x128(*args), name),
+                               bytes_=R * C * (2 + 1 + 4 / 128)))
+        return q, s
+
+    def q_w_dual(w, name, transposed=True):
+        R, C = w.shape
+        q, s = alloc((R, C), torch.uint8), alloc((cdiv(R, 128), cdiv(C, 128)), torch.float32)
+        if transposed:
+            qt, st = alloc((C, R), torch.uint8), alloc((cdiv(C, 128), cdiv(R, 128)), torch.float32)
+            args = (puro.T_WEIGHT, w.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(), q.data_ptr(), s.data_ptr(), stream)
+            launches.append(Launch("quant", name, lambda: check(puro.puro_quant_transpose(*args), name),
+                                   bytes_=R * C * (2 + 2 * (1 + 4 / 16384))))
+            return (q, s), (qt, st)
+        args = (w.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), stream)
+        launches.append(Launch("quant", name, lambda: check(puro.puro_quant_w_128x128(*args), name),
+                               bytes_=R * C * (2 + 1 + 4 / 16384)))
+        return (q, s), None
+
+    def gemm(mode, a, b, out_dtype, name):
+        (aq, sa), (bq, sb) = a, b
+        M, K = aq.shape
+        N = bq.shape[0]
+        out = alloc((M, N), out_dtype)
+        need = puro.puro_gemm_workspace_bytes(mode, M, N, K)
+        ws = alloc((max(need, 16),), torch.uint8)
+        od = puro.OUT_BF16 if out_dtype == torch.bfloat16 else puro.OUT_F32
+        args = (mode, aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), out.data_ptr(), od,
+                M, N, K, ws.data_ptr(), need, stream)
+        flops = 2.0 * M * N * K
+        launches.append(Launch("gemm:" + ("wgrad" if mode == puro.WGRAD else "fprop_dgrad"), name,
+                               lambda: check(puro.puro_gemm_fp8_blockwise(*args), name), flops=flops,
+                               bytes_=M * K + N * K + 4 * M * cdiv(K, 128) + 4 * N * cdiv(K, 128) + M * N * (2 if od else 4)))
+        return out
+
+    if workload == "layer":
+        from workloads import LINEARS
+        for lin in LINEARS:
+            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            xrow, xt = q_act_dual(x, lin + ".quant_x")
+            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            dyrow, dyt = q_act_dual(dy, lin + ".quant_dy")
+            gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
+            gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
+            gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad")
+    elif workload == "qkv_fprop":
+        xrow = q_act(tensors["x"], "quant_x")
+        wrow, _ = q_w_dual(tensors["w"], "quant_w", transposed=False)
+        gemm(puro.FPROP, xrow, wrow, torch.bfloat16, "fprop")
+    elif workload == "mlp_fprop":
+        for lin in ("gate_up", "down"):
+            xrow = q_act(tensors["x_" + lin], lin + ".quant_x")
+            wrow, _ = q_w_dual(tensors["w_" + lin], lin + ".quant_w", transposed=False)
+            gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
+    elif workload == "mlp_down_bwd":
+        dyrow, dyt = q_act_dual(tensors["dy"], "quant_dy")
+        _, wt = q_w_dual(tensors["w"], "quant_w")
+        _, xt = q_act_dual(tensors["x"], "quant_x")
+        gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, "dgrad")
+        gemm(puro.WGRAD, dyt, xt, torch.float32, "wgrad")
+    return launches, keep
+
+
+WORKLOAD_DESC = {
+    "layer": ("Qwen3-1.7B-shaped layer (Puro-2B), 16384 tokens: QKV 2048->4096, O 2048->2048, "
+              "gate_up 2048->12288, down 6144->2048; fprop+dgrad+wgrad and every quantize/transpose kernel"),
+    "qkv_fprop": "QKV projection fprop, 4096 tokens: X[4096x2048] x W[4096x2048]^T -> bf16",
+    "mlp_fprop": "MLP fprop, 8192 tokens: gate_up X[8192x2048] x W[12288x2048]^T, down X[8192x6144] x W[2048x6144]^T",
+    "mlp_down_bwd": "MLP down backward, 8192 tokens: dgrad dY[8192x2048] x W[2048x6144], wgrad dY^T x X[8192x6144]",
+}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_kind):
+    """HBM traffic per launch measured with rocprofv3 counters, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    ent = rec.get("kernels", {}).get(kernel_kind)
+    return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline(tensors, workload, budget_s):
+    """The oracle (as it is) on a bounded sample of the same work, on the host cores:
+    quantize the gate_up (or first) linear's X and W in full, then compute a
+    growing set of sampled fprop outputs until about `budget_s` seconds."""
+    import numpy as np
+    import oracle
+    from workloads import bits
+    oracle.build(force=False)
+    if workload == "layer":
+        x, w = tensors["x_gate_up"], tensors["w_gate_up"]
+    elif workload == "qkv_fprop":
+        x, w = tensors["x"], tensors["w"]
+    elif workload == "mlp_fprop":
+        x, w = tensors["x_gate_up"], tensors["w_gate_up"]
+    else:
+        x, w = tensors["dy"], tensors["w"].T.contiguous()
+    xb, wb = bits(x), bits(w)
+    t0 = time.perf_counter()
+    qa, sa = oracle.quant_act_1x128(xb)
+    qb, sb = oracle.quant_w_128x128(wb)
+    t_quant = time.perf_counter() - t0
+    M, K = qa.shape
+    N = qb.shape[0]
+    rng = np.random.default_rng(0)
+    n = 1024
+    spent = 0.0
+    done_flops = 0.0
+    while spent < budget_s:
+        ms = rng.integers(0, M, n)
+        ns = rng.integers(0, N, n)
+        t1 = time.perf_counter()
+        oracle.gemm_at(oracle.FPROP, qa, sa, qb, sb, ms, ns)
+        dt = time.perf_counter() - t1
+        spent += dt
+        done_flops += 2.0 * n * K
+        if dt < budget_s / 8:
+            n *= 2
+    # scale: quantizing X and W is needed once per full GEMM; charge it in proportion
+    frac = done_flops / (2.0 * M * N * K)
+    total_s = spent + t_quant * frac
+    return {
+        "value": round(done_flops / total_s / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ("fp64 oracle: 1x128/128x128 quantization of the %dx%d activation and %dx%d weight "
+                   "(time charged pro rata) + %d sampled fprop outputs (K=%d), %.1f s" % (M, K, N, K, int(done_flops / (2 * K)), K, total_s)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures the path on one GPU only; --gpus %d is not supported "
+              "(run with --gpus 1)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import blockwise_fp8_gemm_act_amd as puro
+    import workloads
+
+    torch.cuda.set_device(0)
+    tensors = workloads.make(args.workload, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    launches, keep = build_plan(args.workload, tensors, puro, torch)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(tensors, args.workload, args.cpu_seconds)
+
+    def step(events=None):
+        for i, l in enumerate(launches):
+            if events is not None:
+                events[i].record()
+            l.fn()
+        if events is not None:
+            events[len(launches)].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(ev[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+
+    # per-launch durations (event before this launch -> event before the next)
+    per = {}
+    for s in range(args.steps):
+        for i, l in enumerate(launches):
+            d = ev[s][i].elapsed_time(ev[s][i + 1])
+            per.setdefault(i, []).append(d)
+    kinds = {}
+    rows = []
+    for i, l in enumerate(launches):
+        d = sorted(per[i])
+        med = d[len(d) // 2]
+        avg = sum(d) / len(d)
+        k = kinds.setdefault(l.kind, {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "launches": 0})
+        k["ms"] += avg
+        k["flops"] += l.flops
+        k["bytes"] += l.bytes
+        k["launches"] += 1
+        r = {"name": l.name, "ms_avg": round(avg, 4), "ms_med": round(med, 4)}
+        if l.flops:
+            r["tflops"] = round(l.flops / (avg * 1e-3) / 1e12, 1)
+            r["pct_fp8_peak"] = round(100 * l.flops / (avg * 1e-3) / PEAK_FP8_FLOPS, 1)
+        else:
+            r["gbps"] = round(l.bytes / (avg * 1e-3) / 1e9, 1)
+            r["pct_hbm_peak"] = round(100 * l.bytes / (avg * 1e-3) / PEAK_HBM_BPS, 1)
+        rows.append(r)
+
+    gemm_flops = sum(l.flops for l in launches)
+    gemm_ms = sum(v["ms"] for k, v in kinds.items() if k.startswith("gemm"))
+    quant = kinds.get("quant", {"ms": 0.0, "bytes": 0.0})
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the launch type with the most time per step
+    dom_kind, dom = max(((k, v) for k, v in kinds.items()), key=lambda kv: kv[1]["ms"])
+    if dom_kind.startswith("gemm"):
+        achieved = dom["flops"] / (dom["ms"] * 1e-3)
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": PEAK_FP8_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_FLOPS, 4)}
+    else:
+        achieved = dom["bytes"] / (dom["ms"] * 1e-3)
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM_BPS / 1e9,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_BPS, 4)}
+    roof["kernel"] = dom_kind
+    roof["launches_per_step"] = dom["launches"]
+    roof["algorithmic_per_launch"] = (round(dom["flops"] / dom["launches"] / 1e9, 3) if dom_kind.startswith("gemm")
+                                      else round(dom["bytes"] / dom["launches"] / 1e6, 3))
+    roof["algorithmic_unit"] = "GFLOP" if dom_kind.startswith("gemm") else "MB"
+    roof["avg_launch_ms"] = round(dom["ms"] / dom["launches"], 4)
+    tr = load_traffic(dom_kind)
+    roof["traffic"] = tr
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded, Puro-2B-shaped; see workloads.py)",
+        "config": {"workload": WORKLOAD_DESC[args.workload], "name": args.workload,
+                   "tokens": {"layer": 16384, "qkv_fprop": 4096}.get(args.workload, 8192),
+                   "hidden": 2048, "parallelism": "single GPU"},
+        "pct_fp8_peak": round(100 * value * 1e12 / PEAK_FP8_FLOPS, 2),
+        "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
+        "quant_gbps": round(quant["bytes"] / (quant["ms"] * 1e-3) / 1e9, 1) if quant["ms"] else None,
+        "quant_pct_hbm_peak": round(100 * quant["bytes"] / (quant["ms"] * 1e-3) / PEAK_HBM_BPS, 1) if quant["ms"] else None,
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": rows,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -63,6 +63,7 @@ def check_gemm_values(out: np.ndarray, ref: np.ndarray, na: np.ndarray, nb: np.n
         strict = float(np.mean(ulps <= 1)) if ulps.size else 1.0
         assert ok.all(), "%s: %d elements beyond 1 ulp and tolerance; worst norm err %.3g" % (
             what, int((~ok).sum()), worst)
+        return worst, strict
     assert worst <= GEMM_TOL, "%s: normalized error %.3g > %g" % (what, worst, GEMM_TOL)
     return worst, strict
 
