@@ -36,6 +36,7 @@
 namespace puro {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256, kBK = 128;
@@ -107,6 +108,62 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// Writes the 256x256 fp32 accumulator tile (distributed over the 8 waves in
+// the MFMA output layout) to out[M][N] as T (fp32, or bf16 rounded to nearest
+// even), staging rows through LDS so that global stores are 16-byte chunks.
+// `lds` must hold 128 KB and be free; the call begins with a barrier.
+template <typename T>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[4][8], T *out, const GemmArgs &g, int64_t m0,
+                                           int64_t n0, uint8_t *lds, int wm, int wn, int q, int fr) {
+  constexpr int kRowsPerPass = sizeof(T) == 2 ? 128 : 64;     // a multiple of a wave's 64 rows
+  constexpr int kStride = kBN * (int)sizeof(T) + 16;          // padded LDS row (bytes)
+  static_assert(kRowsPerPass * kStride <= 2 * 2 * kSliceBytes, "staging must fit the operand buffers");
+  constexpr int kChunk = 16 / (int)sizeof(T);                  // elements per 16-byte chunk
+  constexpr int kChunksPerRow = kBN / kChunk;
+  const int t = threadIdx.x;
+  const bool vec_ok = (g.N % kChunk) == 0;                      // rows of out are 16-byte aligned
+#pragma unroll
+  for (int pass = 0; pass < kBM / kRowsPerPass; ++pass) {
+    __syncthreads();
+    const int r_lo = pass * kRowsPerPass;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int rb = wm * 64 + mb * 16 + 4 * q;
+      if (rb < r_lo || rb >= r_lo + kRowsPerPass) continue;    // uniform per wave: a wave's 64 rows lie in one pass
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int c = wn * 128 + nb * 16 + fr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[mb][nb][e];
+          T *dst = reinterpret_cast<T *>(lds + (rb + e - r_lo) * kStride + c * (int)sizeof(T));
+          if constexpr (sizeof(T) == 2) *dst = (T)f32_to_bf16_rne(v);
+          else *dst = v;
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int kChunksPerPass = kRowsPerPass * kChunksPerRow;
+#pragma unroll
+    for (int i = 0; i < kChunksPerPass / kThreads; ++i) {
+      const int chunk = t + i * kThreads;
+      const int r = chunk / kChunksPerRow;
+      const int cc = chunk % kChunksPerRow;
+      const int64_t m = m0 + r_lo + r;
+      const int64_t n = n0 + cc * kChunk;
+      if (m >= g.M || n >= g.N) continue;
+      const u32x4 d = *reinterpret_cast<const u32x4 *>(lds + r * kStride + cc * 16);
+      T *dst = out + m * g.N + n;
+      if (vec_ok && n + kChunk <= g.N) {
+        *reinterpret_cast<u32x4 *>(dst) = d;
+      } else {
+        const T *src = reinterpret_cast<const T *>(&d);
+        for (int k = 0; k < kChunk && n + k < g.N; ++k) dst[k] = src[k];
+      }
+    }
+  }
+}
+
 template <bool kRowScaledB, bool kBf16Out, bool kToWs>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
@@ -144,6 +201,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const uint32_t lds0 = lds_addr(&smem[0][0][0]);
   const uint32_t lds_s0 = lds_addr(&sscale[0][0][0]);
   const bool ktail = (K & (kBK - 1)) != 0;
+  const int64_t nb0 = n0 / kBK;                               // first 128-column block of B in this tile
+  const int nb_last = (int)((g.N - 1) / kBK - nb0);           // last valid block, relative to nb0
 
   auto issue_slice = [&](int kb, int buf) {
     const int kofs = kb * kBK;
@@ -182,11 +241,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j)
         dma4_s(src, (uint32_t)min(lane + 64 * j, rows_a - 1) * 4, ls + 256 * j);
     }
-    if (kRowScaledB && w == 1) {
-      const float *src = g.sb + (int64_t)kb * g.N + n0;
+    if (w == 1) {
+      if constexpr (kRowScaledB) {
+        const float *src = g.sb + (int64_t)kb * g.N + n0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma4_s(src, (uint32_t)min(lane + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+        for (int j = 0; j < 4; ++j)
+          dma4_s(src, (uint32_t)min(lane + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+      } else {
+        // block-scaled B: lane l brings sb[n-block nb0 + l][kb] (clamped); lanes 0 and 1
+        // cover the tile's two 128-column blocks
+        const float *src = g.sb + nb0 * g.nk + kb;
+        dma4_s(src, (uint32_t)min(lane, nb_last) * (uint32_t)g.nk * 4, ls + kBM * 4);
+      }
     }
   };
 
@@ -196,8 +262,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const int q = lane >> 4;
   const int p0 = (2 * q) ^ lds_swz(fr);
   const int p1 = p0 ^ 1;
-  const int64_t nbl = min<int64_t>((n0 + wn * 128) / kBK, (g.N - 1) / kBK);   // block-scaled B row of sb
-  const float *sb_row = g.sb + nbl * g.nk;
 
   v4f acc[4][8];
 #pragma unroll
@@ -206,9 +270,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   auto load_frag = [&](const uint8_t *base, int r) -> v8i {
-    const uint4 lo = *reinterpret_cast<const uint4 *>(base + r * kBK + p0 * 16);
-    const uint4 hi = *reinterpret_cast<const uint4 *>(base + r * kBK + p1 * 16);
-    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    const v4i lo = *reinterpret_cast<const v4i *>(base + r * kBK + p0 * 16);
+    const v4i hi = *reinterpret_cast<const v4i *>(base + r * kBK + p1 * 16);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   if (kb_begin < kb_end) issue_slice(kb_begin, 0);
@@ -231,48 +295,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) sa[mb] = *reinterpret_cast<const v4f *>(&lsa[wm * 64 + mb * 16 + 4 * q]);
     if constexpr (!kRowScaledB) {
-      const float sbv = sb_row[kb];
+      const float sbv = lsb[wn];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) sa[mb] *= sbv;
     }
 
-    // Pipeline: the MFMAs of n-block nb are issued while the partials of
-    // n-block nb-1 are promoted, so no FMA waits on the MFMA it reads.
-    v4f P[4];
-    v4f sc[4];
-    {
-      const v8i b0 = load_frag(Bs, wn * 128 + fr);
+    // Software pipeline over the 8 n-blocks of the wave: step nb issues the
+    // 4 MFMAs of n-block nb into one partial bank, prefetches the B fragment
+    // of n-block nb+1, and promotes the other bank (n-block nb-1, whose MFMAs
+    // finished during the previous step) into the accumulators.
+    v4f P[2][4];
+    v8i bf[2];
+    bf[0] = load_frag(Bs, wn * 128 + fr);
+    // row-scaled B: the column scale of n-block nb is read in step nb and used
+    // when n-block nb is promoted, in step nb+1
+    float sb_hold = 1.0f;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mb], b0, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-      if constexpr (kRowScaledB) {
-        const float sbn = lsb[wn * 128 + fr];
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) sc[mb] = sa[mb] * sbn;
-      }
-    }
-#pragma unroll
-    for (int nb = 1; nb <= 8; ++nb) {
+    for (int nb = 0; nb <= 8; ++nb) {
       __builtin_amdgcn_sched_barrier(0);
-      v8i bn;
-      float sbn = 1.0f;
+      const float sbp = sb_hold;                                   // scale of n-block nb-1
+      if (kRowScaledB && nb < 8) sb_hold = lsb[wn * 128 + nb * 16 + fr];
       if (nb < 8) {
-        bn = load_frag(Bs, wn * 128 + nb * 16 + fr);
-        if constexpr (kRowScaledB) sbn = lsb[wn * 128 + nb * 16 + fr];
-      }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if constexpr (kRowScaledB)
-          acc[mb][nb - 1] = __builtin_elementwise_fma(P[mb], sc[mb], acc[mb][nb - 1]);
-        else
-          acc[mb][nb - 1] = __builtin_elementwise_fma(P[mb], sa[mb], acc[mb][nb - 1]);
-        if (nb < 8)
-          P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[mb], bn, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        for (int mb = 0; mb < 4; ++mb)
+          P[nb & 1][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[mb], bf[nb & 1], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (nb + 1 < 8) bf[(nb + 1) & 1] = load_frag(Bs, wn * 128 + (nb + 1) * 16 + fr);
       }
-      if constexpr (kRowScaledB) {
-        if (nb < 8) {
+      if (nb > 0) {
+        const int pb = nb - 1;
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) sc[mb] = sa[mb] * sbn;
+        for (int mb = 0; mb < 4; ++mb) {
+          if constexpr (kRowScaledB) {
+            const v4f ps = P[pb & 1][mb] * sbp;                  // column scale first, in place
+            acc[mb][pb] = __builtin_elementwise_fma(ps, sa[mb], acc[mb][pb]);
+          } else {
+            acc[mb][pb] = __builtin_elementwise_fma(P[pb & 1][mb], sa[mb], acc[mb][pb]);
+          }
+        }
+      }
+      // order within the step: MFMA, the LDS reads of the next n-block (so they
+      // have the whole step to land), then VALU groups between the MFMAs
+      if (nb > 0 && nb < 8) {
+        constexpr int kV = kRowScaledB ? 8 : 4;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
+        if (nb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, kRowScaledB ? 3 : 2, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);                     // VALU
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
         }
       }
     }
@@ -282,29 +354,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows m0 + wm*64 + mb*16 + 4q + e, columns n0 + wn*128 + nb*16 + fr
-  const int64_t mrow0 = m0 + wm * 64 + 4 * q;
-  const int64_t ncol0 = n0 + wn * 128 + fr;
-  const bool full = m0 + kBM <= g.M && n0 + kBN <= g.N;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t m = mrow0 + mb * 16 + e;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int64_t n = ncol0 + nb * 16;
-        if (!full && (m >= g.M || n >= g.N)) continue;
-        const float v = acc[mb][nb][e];
-        if constexpr (kToWs) {
-          g.ws[((int64_t)split * g.M + m) * g.N + n] = v;
-        } else if constexpr (kBf16Out) {
-          reinterpret_cast<uint16_t *>(g.out)[m * g.N + n] = (uint16_t)f32_to_bf16_rne(v);
-        } else {
-          reinterpret_cast<float *>(g.out)[m * g.N + n] = v;
-        }
-      }
-    }
+  // ---- epilogue.  Lane holds rows wm*64 + mb*16 + 4q + e, columns
+  // wn*128 + nb*16 + fr of the tile.  The tile is staged through the (now
+  // idle) LDS in row-major order and leaves as 16-byte row chunks: bf16 in two
+  // passes of 128 rows, fp32 in four passes of 64 rows.
+  if constexpr (kToWs) {
+    store_tile<float>(acc, g.ws + (int64_t)split * g.M * g.N, g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
+  } else if constexpr (kBf16Out) {
+    store_tile<uint16_t>(acc, reinterpret_cast<uint16_t *>(g.out), g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
+  } else {
+    store_tile<float>(acc, reinterpret_cast<float *>(g.out), g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
+  }
 }
 
 // Sum of the split-K partials in increasing split order.
