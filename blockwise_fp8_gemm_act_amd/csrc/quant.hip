@@ -64,14 +64,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
     else
       raw[k] = (u32x4){0u, 0u, 0u, 0u};
   }
-  float f[8][8];
+  // Hide the packed words from the optimizer between phases so that unpacked
+  // values are recomputed in each phase instead of staying live across it.
+  auto refresh = [&]() {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    f[k][0] = bf16lo(raw[k].x); f[k][1] = bf16hi(raw[k].x);
-    f[k][2] = bf16lo(raw[k].y); f[k][3] = bf16hi(raw[k].y);
-    f[k][4] = bf16lo(raw[k].z); f[k][5] = bf16hi(raw[k].z);
-    f[k][6] = bf16lo(raw[k].w); f[k][7] = bf16hi(raw[k].w);
-  }
+    for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(raw[k]));
+  };
+
+  // element (k, c) of the thread's 8x8 block, unpacked where it is used (the
+  // packed words are all that stays live, which keeps occupancy up)
+  auto el = [&](int k, int c) -> float {
+    const uint32_t wd = raw[k][c >> 1];
+    return (c & 1) ? bf16hi(wd) : bf16lo(wd);
+  };
 
   // ---- maxima
   float rmax[8], cmax[8];
@@ -81,9 +86,9 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
   for (int k = 0; k < 8; ++k)
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float v = fabsf(f[k][c]);
+      const float v = fabsf(el(k, c));
       rmax[k] = fmaxf(rmax[k], v);
-      cmax[c] = fmaxf(cmax[c], v);
+      if constexpr (kCol) cmax[c] = fmaxf(cmax[c], v);
     }
 
   TileQ tb;                      // block tile (kBlock)
@@ -160,32 +165,23 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
     bool fast = true;
 #pragma unroll
     for (int k = 0; k < 8; ++k) fast &= rs[k] >= kFastDivMinScale;
-    u32x2 out[8];
-    if (fast) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float v[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = quot_fast(f[k][c], rs[k], rr[k]);
-        out[k].x = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        out[k].y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const bool fk = rs[k] >= kFastDivMinScale;
-        float v[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = fk ? quot_fast(f[k][c], rs[k], rr[k]) : f[k][c] / rs[k];
-        out[k].x = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        out[k].y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-      }
-    }
+    refresh();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      float v[8];
+      if (fast) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = quot_fast(el(k, c), rs[k], rr[k]);
+      } else {
+        const bool fk = rs[k] >= kFastDivMinScale;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = fk ? quot_fast(el(k, c), rs[k], rr[k]) : el(k, c) / rs[k];
+      }
+      u32x2 o;
+      o.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+      o.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
       const int64_t r = r0 + k;
-      if (cvalid && r < a.R)
-        __builtin_nontemporal_store(out[k], reinterpret_cast<u32x2 *>(a.q + r * a.C + c0));
+      if (cvalid && r < a.R) __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(a.q + r * a.C + c0));
     }
   }
 
@@ -208,33 +204,25 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
     bool fast = true;
 #pragma unroll
     for (int c = 0; c < 8; ++c) fast &= cs[c] >= kFastDivMinScale;
-    u32x2 col[8];
-    if (fast) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = quot_fast(f[k][c], cs[c], cr[c]);
-        col[c].x = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        col[c].y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bool fc = cs[c] >= kFastDivMinScale;
-        float v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = fc ? quot_fast(f[k][c], cs[c], cr[c]) : f[k][c] / cs[c];
-        col[c].x = pack4_e4m3(v[0], v[1], v[2], v[3]);
-        col[c].y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-      }
-    }
+    refresh();
     // LDS row c (a column of the block) holds 16 slots of 8 codes (8 rows);
     // slot rg is stored at physical slot rg ^ (c / 8).
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
+      float v[8];
+      if (fast) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = quot_fast(el(k, c), cs[c], cr[c]);
+      } else {
+        const bool fc = cs[c] >= kFastDivMinScale;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = fc ? quot_fast(el(k, c), cs[c], cr[c]) : el(k, c) / cs[c];
+      }
+      u32x2 col;
+      col.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+      col.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
       const int lc = cc * 8 + c;
-      *reinterpret_cast<u32x2 *>(&lds_t[lc * kTile + ((rg ^ cc) * 8)]) = col[c];
+      *reinterpret_cast<u32x2 *>(&lds_t[lc * kTile + ((rg ^ cc) * 8)]) = col;
     }
     __syncthreads();
 #pragma unroll
