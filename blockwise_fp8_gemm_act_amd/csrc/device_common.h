@@ -17,6 +17,7 @@ namespace puro {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 128;          // tile edge (elements)
 constexpr float kE4m3Max = 448.0f;  // largest finite OCP E4M3FN value
@@ -84,6 +85,36 @@ __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
   return v;
+}
+
+// Magnitude bits of the two bf16 values packed in a word.  For finite values
+// the magnitude bits order exactly like the magnitudes, so maxima can be taken
+// on them as 16-bit integers (packed max) and turned into a float at the end:
+// the fp32 value of a bf16 magnitude m is the bit pattern m << 16.
+__device__ __forceinline__ u16x2 bf16_mags(uint32_t w) {
+  return __builtin_bit_cast(u16x2, w & 0x7fff7fffu);
+}
+__device__ __forceinline__ u16x2 max16x2(u16x2 a, u16x2 b) { return __builtin_elementwise_max(a, b); }
+__device__ __forceinline__ uint32_t hmax16(u16x2 a) { return a.x > a.y ? a.x : a.y; }
+__device__ __forceinline__ float mag_to_float(uint32_t m) { return __uint_as_float(m << 16); }
+
+// Max over the 16 lanes of a DPP row of non-negative integers.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false));  // row_ror:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false));  // row_ror:1
+  return v;
+}
+
+// Max over a whole wave of 64 lanes of non-negative integers, returned uniformly.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = row16_max_u32(v);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
 }
 
 // Max over a whole wave of 64 lanes, returned uniformly.

@@ -78,38 +78,46 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
     return (c & 1) ? bf16hi(wd) : bf16lo(wd);
   };
 
-  // ---- maxima
-  float rmax[8], cmax[8];
+  // ---- maxima, on the packed magnitude bits (see bf16_mags)
+  uint32_t rbits[8];                 // row maxima of this thread's 8 columns
+  u16x2 cbits[4];                    // column maxima over this thread's 8 rows (column pairs)
 #pragma unroll
-  for (int k = 0; k < 8; ++k) { rmax[k] = 0.0f; cmax[k] = 0.0f; }
+  for (int j = 0; j < 4; ++j) cbits[j] = (u16x2){0, 0};
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float v = fabsf(el(k, c));
-      rmax[k] = fmaxf(rmax[k], v);
-      if constexpr (kCol) cmax[c] = fmaxf(cmax[c], v);
+  for (int k = 0; k < 8; ++k) {
+    const u16x2 m0 = bf16_mags(raw[k].x), m1 = bf16_mags(raw[k].y);
+    const u16x2 m2 = bf16_mags(raw[k].z), m3 = bf16_mags(raw[k].w);
+    rbits[k] = hmax16(max16x2(max16x2(m0, m1), max16x2(m2, m3)));
+    if constexpr (kCol) {
+      cbits[0] = max16x2(cbits[0], m0);
+      cbits[1] = max16x2(cbits[1], m1);
+      cbits[2] = max16x2(cbits[2], m2);
+      cbits[3] = max16x2(cbits[3], m3);
     }
+  }
 
   TileQ tb;                      // block tile (kBlock)
   if constexpr (kBlock) {
-    float m = 0.0f;
+    uint32_t m = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) m = fmaxf(m, rmax[k]);
-    m = wave_max(m);
-    if ((t & 63) == 0) lds_wmax[t >> 6] = m;
+    for (int k = 0; k < 8; ++k) m = max(m, rbits[k]);
+    m = wave_max_u32(m);
+    if ((t & 63) == 0) lds_wmax[t >> 6] = mag_to_float(m);
   }
   if constexpr (kRow) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rmax[k] = row16_max(rmax[k]);
+    for (int k = 0; k < 8; ++k) rbits[k] = row16_max_u32(rbits[k]);
     if (cc == 0) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) lds_rowamax[rg * 8 + k] = rmax[k];
+      for (int k = 0; k < 8; ++k) lds_rowamax[rg * 8 + k] = mag_to_float(rbits[k]);
     }
   }
   if constexpr (kCol) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lds_part[rg * kTile + cc * 8 + c] = cmax[c];
+    for (int j = 0; j < 4; ++j) {
+      lds_part[rg * kTile + cc * 8 + 2 * j] = mag_to_float(cbits[j].x);
+      lds_part[rg * kTile + cc * 8 + 2 * j + 1] = mag_to_float(cbits[j].y);
+    }
   }
   __syncthreads();
 
