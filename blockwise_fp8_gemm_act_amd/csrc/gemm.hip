@@ -23,6 +23,9 @@
 //  - one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 16x16 block of one
 //    slice, so its result is the slice partial P_kb; it is promoted at once:
 //    acc = fma(P, sA*sB, acc);
+//  - the barrier that publishes slice kb+1 sits before the last of slice kb's
+//    eight n-block steps, so the next slice's fragment and scale reads overlap
+//    MFMAs instead of stalling all waves at once at the slice boundary;
 //  - LDS rows are 128 B; the 16-byte chunk c of row r sits at chunk
 //    c ^ ((r & 7) ^ ((r >> 3) & 1)), which makes the fragment reads (16 lanes
 //    reading one chunk column of 16 consecutive rows) bank-conflict free;
@@ -32,6 +35,8 @@
 //    kernel sums in a fixed order (deterministic).
 #include "device_common.h"
 #include "launch.h"
+
+#include <type_traits>
 
 namespace puro {
 
@@ -203,57 +208,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const bool ktail = (K & (kBK - 1)) != 0;
   const int64_t nb0 = n0 / kBK;                               // first 128-column block of B in this tile
   const int nb_last = (int)((g.N - 1) / kBK - nb0);           // last valid block, relative to nb0
+  // Interior tiles: the lane offset is rig*K + logical chunk and the row
+  // group and K slice go into the scalar base, so A and B share two VGPRs.
+  const uint32_t voff0 = (uint32_t)(rig * K + kc0);
+  const uint32_t voff1 = (uint32_t)(rig * K + kc1);
+  const bool full_rows = rows_a == kBM && rows_b == kBN;
+
+  // Per-lane values that only edge tiles, the ragged last slice and the scale
+  // copies need are recomputed from an opaque lane id at each call, so that
+  // they occupy no VGPRs across the K loop.
+  auto issue_scales = [&](int kb, int buf) {
+    // wave 0 copies sA rows m0..m0+255; wave 1 copies sB columns n0.. (row-scaled
+    // B) or the tile's two block scales (block-scaled B)
+    if (w > 1) return;
+    const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
+    int ln = __lane_id();
+    asm volatile("" : "+v"(ln));
+    if (w == 0) {
+      const float *src = g.sa + (int64_t)kb * g.M + m0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, rows_a - 1) * 4, ls + 256 * j);
+    } else if constexpr (kRowScaledB) {
+      const float *src = g.sb + (int64_t)kb * g.N + n0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+    } else {
+      // lane l brings sb[n-block nb0 + l][kb] (clamped); lanes 0 and 1 cover
+      // the tile's two 128-column blocks
+      const float *src = g.sb + nb0 * g.nk + kb;
+      dma4_s(src, (uint32_t)min(ln, nb_last) * (uint32_t)g.nk * 4, ls + kBM * 4);
+    }
+  };
 
   auto issue_slice = [&](int kb, int buf) {
     const int kofs = kb * kBK;
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const uint32_t lb = la + kSliceBytes;
-    if (!(ktail && kb == g.nk - 1)) {
+    if (full_rows && !(ktail && kb == g.nk - 1)) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int grp = w * 4 + j;
-        const int r = grp * 8 + rig;
-        const int kc = (j & 1) ? kc1 : kc0;
-        const uint32_t offa = (r < rows_a ? r * K : 0) + kc;
-        const uint32_t offb = (r < rows_b ? r * K : 0) + kc;
-        dma16_s(a_tile + kofs, offa, la + grp * 1024);
-        dma16_s(b_tile + kofs, offb, lb + grp * 1024);
+        const int64_t rofs = (int64_t)grp * 8 * g.K + kofs;
+        dma16_s(a_tile + rofs, (j & 1) ? voff1 : voff0, la + grp * 1024);
+        dma16_s(b_tile + rofs, (j & 1) ? voff1 : voff0, lb + grp * 1024);
       }
     } else {
-      // ragged last slice: chunks at or past K read a zero page
+      // edge tiles and the ragged last slice: chunks at or past K read a zero page
+      int ln = __lane_id();
+      asm volatile("" : "+v"(ln));
+      const int rg = ln >> 3;
+      const int k0 = ((ln & 7) ^ rg) * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int grp = w * 4 + j;
-        const int r = grp * 8 + rig;
-        const int kc = (j & 1) ? kc1 : kc0;
+        const int r = grp * 8 + rg;
+        const int kc = (j & 1) ? (k0 ^ 16) : k0;
         const bool kin = kofs + kc < K;
-        const uint8_t *pa = kin ? a_tile + kofs + (r < rows_a ? r * K : 0) + kc : g_zero16;
-        const uint8_t *pb = kin ? b_tile + kofs + (r < rows_b ? r * K : 0) + kc : g_zero16;
+        const uint8_t *pa = kin ? a_tile + kofs + (r < rows_a ? (int64_t)r * K : 0) + kc : g_zero16;
+        const uint8_t *pb = kin ? b_tile + kofs + (r < rows_b ? (int64_t)r * K : 0) + kc : g_zero16;
         dma16_v(pa, la + grp * 1024);
         dma16_v(pb, lb + grp * 1024);
       }
     }
-    // scales: wave 0 copies sA rows m0..m0+255, wave 1 (row-scaled B only) sB columns n0..
-    const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
-    if (w == 0) {
-      const float *src = g.sa + (int64_t)kb * g.M + m0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dma4_s(src, (uint32_t)min(lane + 64 * j, rows_a - 1) * 4, ls + 256 * j);
-    }
-    if (w == 1) {
-      if constexpr (kRowScaledB) {
-        const float *src = g.sb + (int64_t)kb * g.N + n0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          dma4_s(src, (uint32_t)min(lane + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
-      } else {
-        // block-scaled B: lane l brings sb[n-block nb0 + l][kb] (clamped); lanes 0 and 1
-        // cover the tile's two 128-column blocks
-        const float *src = g.sb + nb0 * g.nk + kb;
-        dma4_s(src, (uint32_t)min(lane, nb_last) * (uint32_t)g.nk * 4, ls + kBM * 4);
-      }
-    }
+    issue_scales(kb, buf);
   };
 
   // ---- fragment read plan: lane reads row (lane % 16) of each 16-row block,
@@ -275,83 +292,119 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  if (kb_begin < kb_end) issue_slice(kb_begin, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const int buf = (kb - kb_begin) & 1;
-    if (kb + 1 < kb_end) issue_slice(kb + 1, buf ^ 1);
-
-    const uint8_t *As = smem[buf][0];
-    const uint8_t *Bs = smem[buf][1];
+  // ---- K loop.  Slice kb is computed from buffer (kb - kb_begin) & 1 while
+  // slice kb+1 is copied into the other one.  The barrier that publishes slice
+  // kb+1 sits before the last n-block step of slice kb, so that the reads of
+  // slice kb+1's A fragments, first B fragment and scales overlap the MFMAs of
+  // that step instead of stalling every wave at the start of the slice.
+  v8i af[4];                 // A fragments of the wave's 4 m-blocks
+  v8i bf[2];                 // B fragments of n-blocks nb (in use) and nb+1 (landing)
+  v4f sa[4];                 // row scales sA of the lane's 4 rows in each m-block
+  float sbn0 = 1.0f;         // row-scaled B: column scale of the coming slice's n-block 0
+  float sbk = 1.0f;          // block-scaled B: the coming slice's scale of the wave's 128 columns
+  auto load_scales = [&](int buf) {
     const float *lsa = sscale[buf][0];
     const float *lsb = sscale[buf][1];
-
-    v8i af[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) af[mb] = load_frag(As, wm * 64 + mb * 16 + fr);
-    v4f sa[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) sa[mb] = *reinterpret_cast<const v4f *>(&lsa[wm * 64 + mb * 16 + 4 * q]);
-    if constexpr (!kRowScaledB) {
-      const float sbv = lsb[wn];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sa[mb] *= sbv;
-    }
+    if constexpr (kRowScaledB) sbn0 = lsb[wn * 128 + fr];
+    else sbk = lsb[wn];
+  };
 
-    // Software pipeline over the 8 n-blocks of the wave: step nb issues the
-    // 4 MFMAs of n-block nb into one partial bank, prefetches the B fragment
-    // of n-block nb+1, and promotes the other bank (n-block nb-1, whose MFMAs
-    // finished during the previous step) into the accumulators.
-    v4f P[2][4];
-    v8i bf[2];
-    bf[0] = load_frag(Bs, wn * 128 + fr);
-    // row-scaled B: the column scale of n-block nb is read in step nb and used
-    // when n-block nb is promoted, in step nb+1
-    float sb_hold = 1.0f;
+  if (kb_begin < kb_end) {
+    issue_slice(kb_begin, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    bf[0] = load_frag(smem[0][1], wn * 128 + fr);
 #pragma unroll
-    for (int nb = 0; nb <= 8; ++nb) {
+    for (int mb = 0; mb < 4; ++mb) af[mb] = load_frag(smem[0][0], wm * 64 + mb * 16 + fr);
+    load_scales(0);
+  }
+
+  // One slice.  Step nb issues the 4 MFMAs of n-block nb; the partial of
+  // n-block nb-1 is promoted into the accumulators from P[mb] right before
+  // MFMA (nb, mb) overwrites it, and the B fragment of n-block nb+1 is read
+  // one step ahead.  kNext: a slice follows in this work item.
+  auto slice = [&](int kb, auto next_c) {
+    constexpr bool kNext = decltype(next_c)::value;
+    const int buf = (kb - kb_begin) & 1;
+    const uint8_t *Bs = smem[buf][1];
+    const float *lsb = sscale[buf][1];
+    v4f P[4];
+    float sbv[8];              // row-scaled B: column scale of each n-block
+    sbv[0] = sbn0;
+    v4f sc[4];                 // block-scaled B: promotion factors sA * sB
+    // the buffer of slice kb-1 was released by the barrier inside slice kb-1
+    if constexpr (kNext) issue_slice(kb + 1, buf ^ 1);
+    auto promote = [&](int pb, int mb) {
+      if constexpr (kRowScaledB) {
+        const v4f ps = P[mb] * sbv[pb];                          // column scale first, in place
+        acc[mb][pb] = __builtin_elementwise_fma(ps, sa[mb], acc[mb][pb]);
+      } else {
+        acc[mb][pb] = __builtin_elementwise_fma(P[mb], sc[mb], acc[mb][pb]);
+      }
+    };
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
       __builtin_amdgcn_sched_barrier(0);
-      const float sbp = sb_hold;                                   // scale of n-block nb-1
-      if (kRowScaledB && nb < 8) sb_hold = lsb[wn * 128 + nb * 16 + fr];
-      if (nb < 8) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          P[nb & 1][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af[mb], bf[nb & 1], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        if (nb + 1 < 8) bf[(nb + 1) & 1] = load_frag(Bs, wn * 128 + (nb + 1) * 16 + fr);
+      if (nb == 7) {
+        // Every wave holds its n-block 7 fragment (lgkmcnt) and has landed its
+        // share of slice kb+1 (vmcnt): past the barrier slice kb+1 is readable
+        // and nothing reads slice kb's buffer any more.
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (nb > 0) {
-        const int pb = nb - 1;
+      if (kRowScaledB && nb + 1 < 8) sbv[nb + 1] = lsb[wn * 128 + (nb + 1) * 16 + fr];
+      if (nb + 1 < 8) bf[(nb + 1) & 1] = load_frag(Bs, wn * 128 + (nb + 1) * 16 + fr);
+      if (nb == 7 && kNext) bf[0] = load_frag(smem[buf ^ 1][1], wn * 128 + fr);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if constexpr (kRowScaledB) {
-            const v4f ps = P[pb & 1][mb] * sbp;                  // column scale first, in place
-            acc[mb][pb] = __builtin_elementwise_fma(ps, sa[mb], acc[mb][pb]);
-          } else {
-            acc[mb][pb] = __builtin_elementwise_fma(P[pb & 1][mb], sa[mb], acc[mb][pb]);
-          }
+      for (int mb = 0; mb < 4; ++mb) {
+        if (nb > 0) promote(nb - 1, mb);
+        P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            af[mb], bf[nb & 1], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (nb == 7 && kNext) af[mb] = load_frag(smem[buf ^ 1][0], wm * 64 + mb * 16 + fr);
+        if (nb == 0 && !kRowScaledB) sc[mb] = sa[mb] * sbk;
+      }
+      // issue order within the step: LDS reads first (a whole step to land),
+      // then VALU groups between the MFMAs
+      constexpr int kV = kRowScaledB ? 8 : 4;
+      constexpr int kS = kRowScaledB ? 1 : 0;
+      if (nb == 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);                // LDS reads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+          if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
         }
-      }
-      // order within the step: MFMA, the LDS reads of the next n-block (so they
-      // have the whole step to land), then VALU groups between the MFMAs
-      if (nb > 0 && nb < 8) {
-        constexpr int kV = kRowScaledB ? 8 : 4;
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                      // MFMA
-        if (nb + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, kRowScaledB ? 3 : 2, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);                     // VALU
+      } else if (nb < 7) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+      } else {
+        if (kNext) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (kNext) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) promote(7, mb);
+    if constexpr (kNext) load_scales(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  {
+    int kb = kb_begin;
+    for (; kb + 1 < kb_end; ++kb) slice(kb, std::true_type{});
+    if (kb < kb_end) slice(kb, std::false_type{});
   }
 
   // ---- epilogue.  Lane holds rows wm*64 + mb*16 + 4q + e, columns
@@ -401,12 +454,26 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
   p.tiles_n = (int)((N + kBN - 1) / kBN);
   p.splits = 1;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
-  // Too few output tiles to occupy the 256 compute units: split the K loop,
-  // keeping at least 8 slices per split.
+  // Split the K loop when the output tiles fill the 256 compute units poorly
+  // (a last round of tiles that leaves units idle, or fewer tiles than units).
+  // Estimated time with s splits: rounds of 256 work items, each of ceil(nk/s)
+  // slices plus about 2 slices of fixed cost (first copy, epilogue) at about
+  // 1.9 us per slice, plus the workspace traffic (every split writes an fp32
+  // partial of the output and the reduction reads it back) at about 4 TB/s.
+  // More splits must win by 3%; at least 4 slices per split.
   if (tiles > 0 && p.nk > 0) {
-    int s = 1;
-    while (tiles * s < 256 && p.nk / (2 * s) >= 8 && s < 8) s *= 2;
-    p.splits = s;
+    double best = 0.0;
+    for (int s = 1; s <= 8; ++s) {
+      const int spl = (p.nk + s - 1) / s;
+      if (s > 1 && (spl < 4 || (p.nk + spl - 1) / spl != s)) continue;
+      const double rounds = (double)((tiles * s + 255) / 256);
+      const double t = rounds * (spl + 2) * 1.9e-6 +
+                       (s > 1 ? 2.0 * s * (double)M * (double)N * 4.0 / 4.0e12 : 0.0);
+      if (s == 1 || t < best * 0.97) {
+        best = t;
+        p.splits = s;
+      }
+    }
   }
   p.spl = (p.nk + p.splits - 1) / p.splits;
   if (p.spl > 0) p.splits = (p.nk + p.spl - 1) / p.spl;
