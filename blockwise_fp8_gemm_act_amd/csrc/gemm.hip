@@ -109,6 +109,46 @@ __device__ __forceinline__ void dma4_s(const void *sbase, uint32_t voff, uint32_
       : "memory");
 }
 
+// The 8 copies of one interior slice for this wave: row groups 4w+j (j = 0..3)
+// of A and of B.  Lane offsets vj already include row group j; the 64-bit
+// bases point at the wave's first row group in the slice; A lands at `lds`
+// + 1024 j and B at `lds` + 32 KB + 1024 j.  M0 is saved once and stepped
+// with scalar adds.
+__device__ __forceinline__ void dma_slice8(const void *abase, const void *bbase, uint32_t v0, uint32_t v1,
+                                           uint32_t v2, uint32_t v3, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %6\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %6\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %6\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(abase), "s"(bbase), "s"(lds)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -208,11 +248,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const bool ktail = (K & (kBK - 1)) != 0;
   const int64_t nb0 = n0 / kBK;                               // first 128-column block of B in this tile
   const int nb_last = (int)((g.N - 1) / kBK - nb0);           // last valid block, relative to nb0
-  // Interior tiles: the lane offset is rig*K + logical chunk and the row
-  // group and K slice go into the scalar base, so A and B share two VGPRs.
+  // Interior tiles: lane offsets (row group j, row rig, logical chunk) are
+  // shared by A and B; the wave's first row group and the K slice go into the
+  // scalar bases.  Scales travel as one 16-byte-per-lane copy when their rows
+  // are 16-byte aligned.
   const uint32_t voff0 = (uint32_t)(rig * K + kc0);
-  const uint32_t voff1 = (uint32_t)(rig * K + kc1);
+  const uint32_t voff1 = (uint32_t)((8 + rig) * K + kc1);
+  const uint32_t voff2 = (uint32_t)((16 + rig) * K + kc0);
+  const uint32_t voff3 = (uint32_t)((24 + rig) * K + kc1);
   const bool full_rows = rows_a == kBM && rows_b == kBN;
+  const bool scale_x4 = full_rows && (g.M & 3) == 0 && (!kRowScaledB || (g.N & 3) == 0);
+  const uint8_t *a_wave = a_tile + (int64_t)(w * 32) * g.K;
+  const uint8_t *b_wave = b_tile + (int64_t)(w * 32) * g.K;
 
   // Per-lane values that only edge tiles, the ragged last slice and the scale
   // copies need are recomputed from an opaque lane id at each call, so that
@@ -224,6 +271,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
+    if (scale_x4 && (w == 0 || kRowScaledB)) {
+      // lane l brings the 4 scales of rows (or columns) 4l .. 4l+3
+      const float *src = w == 0 ? g.sa + (int64_t)kb * g.M + m0 : g.sb + (int64_t)kb * g.N + n0;
+      dma16_s(src, (uint32_t)ln * 16, ls + (w == 0 ? 0 : kBM * 4));
+      return;
+    }
     if (w == 0) {
       const float *src = g.sa + (int64_t)kb * g.M + m0;
 #pragma unroll
@@ -245,13 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const uint32_t lb = la + kSliceBytes;
     if (full_rows && !(ktail && kb == g.nk - 1)) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int grp = w * 4 + j;
-        const int64_t rofs = (int64_t)grp * 8 * g.K + kofs;
-        dma16_s(a_tile + rofs, (j & 1) ? voff1 : voff0, la + grp * 1024);
-        dma16_s(b_tile + rofs, (j & 1) ? voff1 : voff0, lb + grp * 1024);
-      }
+      dma_slice8(a_wave + kofs, b_wave + kofs, voff0, voff1, voff2, voff3, la + w * 4096);
     } else {
       // edge tiles and the ragged last slice: chunks at or past K read a zero page
       int ln = __lane_id();
