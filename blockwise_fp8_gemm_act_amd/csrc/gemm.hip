@@ -27,8 +27,10 @@
 //    eight n-block steps, so the next slice's fragment and scale reads overlap
 //    MFMAs instead of stalling all waves at once at the slice boundary;
 //  - LDS rows are 128 B; the 16-byte chunk c of row r sits at chunk
-//    c ^ ((r & 7) ^ ((r >> 3) & 1)), which makes the fragment reads (16 lanes
-//    reading one chunk column of 16 consecutive rows) bank-conflict free;
+//    c ^ swz(r), swz(r) = r1 | r3 << 1 | (r2 ^ r4) << 2 (ri: bit i of r),
+//    which keeps both fragment read patterns (16 lanes reading one chunk
+//    column of 16 consecutive A rows, or of the 16 B rows 8a + b, a, b < 4)
+//    bank-conflict free;
 //  - rows past M or N are read from clamped (valid) rows and never stored;
 //    K chunks past K read a 16-byte zero page, so a ragged last slice adds 0;
 //  - optional split-K writes fp32 partials to a workspace that a second
@@ -64,7 +66,6 @@ struct GemmArgs {
   int spl;         // slices per split
 };
 
-__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Global -> LDS DMA (gfx950 global_load_lds).  The LDS destination of lane i
 // is M0 + 16*i (dwordx4) or M0 + 4*i (dword); M0 is set and restored inside
@@ -153,62 +154,36 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// Writes the 256x256 fp32 accumulator tile (distributed over the 8 waves in
-// the MFMA output layout) to out[M][N] as T (fp32, or bf16 rounded to nearest
-// even), staging rows through LDS so that global stores are 16-byte chunks.
-// `lds` must hold 128 KB and be free; the call begins with a barrier.
-template <typename T>
-__device__ __forceinline__ void store_tile(const v4f (&acc)[4][8], T *out, const GemmArgs &g, int64_t m0,
-                                           int64_t n0, uint8_t *lds, int wm, int wn, int q, int fr) {
-  constexpr int kRowsPerPass = sizeof(T) == 2 ? 128 : 64;     // a multiple of a wave's 64 rows
-  constexpr int kStride = kBN * (int)sizeof(T) + 16;          // padded LDS row (bytes)
-  static_assert(kRowsPerPass * kStride <= 2 * 2 * kSliceBytes, "staging must fit the operand buffers");
-  constexpr int kChunk = 16 / (int)sizeof(T);                  // elements per 16-byte chunk
-  constexpr int kChunksPerRow = kBN / kChunk;
-  const int t = threadIdx.x;
-  const bool vec_ok = (g.N % kChunk) == 0;                      // rows of out are 16-byte aligned
-#pragma unroll
-  for (int pass = 0; pass < kBM / kRowsPerPass; ++pass) {
-    __syncthreads();
-    const int r_lo = pass * kRowsPerPass;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int rb = wm * 64 + mb * 16 + 4 * q;
-      if (rb < r_lo || rb >= r_lo + kRowsPerPass) continue;    // uniform per wave: a wave's 64 rows lie in one pass
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int c = wn * 128 + nb * 16 + fr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = acc[mb][nb][e];
-          T *dst = reinterpret_cast<T *>(lds + (rb + e - r_lo) * kStride + c * (int)sizeof(T));
-          if constexpr (sizeof(T) == 2) *dst = (T)f32_to_bf16_rne(v);
-          else *dst = v;
-        }
-      }
-    }
-    __syncthreads();
-    constexpr int kChunksPerPass = kRowsPerPass * kChunksPerRow;
-#pragma unroll
-    for (int i = 0; i < kChunksPerPass / kThreads; ++i) {
-      const int chunk = t + i * kThreads;
-      const int r = chunk / kChunksPerRow;
-      const int cc = chunk % kChunksPerRow;
-      const int64_t m = m0 + r_lo + r;
-      const int64_t n = n0 + cc * kChunk;
-      if (m >= g.M || n >= g.N) continue;
-      const u32x4 d = *reinterpret_cast<const u32x4 *>(lds + r * kStride + cc * 16);
-      T *dst = out + m * g.N + n;
-      if (vec_ok && n + kChunk <= g.N) {
-        *reinterpret_cast<u32x4 *>(dst) = d;
-      } else {
-        const T *src = reinterpret_cast<const T *>(&d);
-        for (int k = 0; k < kChunk && n + k < g.N; ++k) dst[k] = src[k];
-      }
-    }
-  }
+// One work item: a 256x256 output tile and one split of its K slices.  All
+// fields are uniform across the workgroup.
+struct Tile {
+  int m0, n0;                // first row of A / of B (M, N < 2^31)
+  int kb_begin, kb_end;
+  int rows_a, rows_b;        // valid rows of A / B in the tile
+  int split;
+};
+
+__device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item) {
+  const int total_tiles = g.tiles_m * g.tiles_n;
+  Tile t;
+  t.split = item / total_tiles;
+  const int tile = item - t.split * total_tiles;
+  const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
+  const int tn = tile / g.tiles_m;
+  t.m0 = tm * kBM;
+  t.n0 = tn * kBN;
+  t.kb_begin = t.split * g.spl;
+  t.kb_end = min(g.nk, t.kb_begin + g.spl);
+  t.rows_a = min((int)g.M - t.m0, kBM);
+  t.rows_b = min((int)g.N - t.n0, kBN);
+  return t;
 }
 
+// Persistent kernel: workgroup b computes work items b, b + G, b + 2G, ...
+// (G = gridDim.x, at most one workgroup per compute unit), treating their K
+// slices as one stream: the first slice of the next item is copied while the
+// last slice of the current one is computed, and the current item's output
+// leaves with direct global stores that drain while the next item computes.
 template <bool kRowScaledB, bool kBf16Out, bool kToWs>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
@@ -219,113 +194,116 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
-
-  const int total_tiles = g.tiles_m * g.tiles_n;
-  const int bid = blockIdx.x;
-  const int split = bid / total_tiles;
-  const int tile = bid - split * total_tiles;
-  const int tm = tile % g.tiles_m;       // consecutive workgroups walk down M: they share B
-  const int tn = tile / g.tiles_m;
-  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
-  const int kb_begin = split * g.spl;
-  const int kb_end = min(g.nk, kb_begin + g.spl);
+  const int total_items = g.tiles_m * g.tiles_n * g.splits;
+  int item = blockIdx.x;
+  if (item >= total_items) return;
   const int K = (int)g.K;
+  const bool ktail = (K & (kBK - 1)) != 0;
 
   // ---- global -> LDS copy plan.  Wave w fills LDS row groups grp = 4w + j
   // (j = 0..3) of 8 rows; lane -> row grp*8 + (lane/8), physical chunk lane%8,
-  // whose logical chunk is (lane%8) ^ (lane/8) ^ (j&1).  Rows past M / N are
+  // whose logical chunk is (lane%8) ^ swz(row).  Rows past M / N are
   // redirected to the tile's first row (finite codes whose products are
   // never stored).
   const int rig = lane >> 3;
-  const int kc0 = ((lane & 7) ^ rig) * 16;     // even j
-  const int kc1 = kc0 ^ 16;                     // odd j
-  const uint8_t *a_tile = g.a + m0 * g.K;
-  const uint8_t *b_tile = g.b + n0 * g.K;
-  const int rows_a = (int)min<int64_t>(g.M - m0, kBM);   // valid rows in this tile
-  const int rows_b = (int)min<int64_t>(g.N - n0, kBN);
+  auto dma_chunk = [](int ln, int j) {          // logical chunk (bytes) of lane ln in group j
+    const int rg = ln >> 3;
+    return ((ln & 7) ^ (((rg >> 1) & 1) | ((j & 1) << 1) | ((((rg >> 2) ^ (j >> 1)) & 1) << 2))) * 16;
+  };
   const uint32_t lds0 = lds_addr(&smem[0][0][0]);
   const uint32_t lds_s0 = lds_addr(&sscale[0][0][0]);
-  const bool ktail = (K & (kBK - 1)) != 0;
-  const int64_t nb0 = n0 / kBK;                               // first 128-column block of B in this tile
-  const int nb_last = (int)((g.N - 1) / kBK - nb0);           // last valid block, relative to nb0
   // Interior tiles: lane offsets (row group j, row rig, logical chunk) are
   // shared by A and B; the wave's first row group and the K slice go into the
-  // scalar bases.  Scales travel as one 16-byte-per-lane copy when their rows
-  // are 16-byte aligned.
-  const uint32_t voff0 = (uint32_t)(rig * K + kc0);
-  const uint32_t voff1 = (uint32_t)((8 + rig) * K + kc1);
-  const uint32_t voff2 = (uint32_t)((16 + rig) * K + kc0);
-  const uint32_t voff3 = (uint32_t)((24 + rig) * K + kc1);
-  const bool full_rows = rows_a == kBM && rows_b == kBN;
-  const bool scale_x4 = full_rows && (g.M & 3) == 0 && (!kRowScaledB || (g.N & 3) == 0);
-  const uint8_t *a_wave = a_tile + (int64_t)(w * 32) * g.K;
-  const uint8_t *b_wave = b_tile + (int64_t)(w * 32) * g.K;
+  // scalar bases.
+  const uint32_t voff0 = (uint32_t)(rig * K + dma_chunk(lane, 0));
+  const uint32_t voff1 = (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
+  const uint32_t voff2 = (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
+  const uint32_t voff3 = (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
 
   // Per-lane values that only edge tiles, the ragged last slice and the scale
   // copies need are recomputed from an opaque lane id at each call, so that
   // they occupy no VGPRs across the K loop.
-  auto issue_scales = [&](int kb, int buf) {
+  auto issue_scales = [&](const Tile &tl, int kb, int buf) {
     // wave 0 copies sA rows m0..m0+255; wave 1 copies sB columns n0.. (row-scaled
     // B) or the tile's two block scales (block-scaled B)
     if (w > 1) return;
     const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
-    if (scale_x4 && (w == 0 || kRowScaledB)) {
-      // lane l brings the 4 scales of rows (or columns) 4l .. 4l+3
-      const float *src = w == 0 ? g.sa + (int64_t)kb * g.M + m0 : g.sb + (int64_t)kb * g.N + n0;
+    const bool full = tl.rows_a == kBM && tl.rows_b == kBN;
+    if (full && (g.M & 3) == 0 && (!kRowScaledB || (g.N & 3) == 0) && (w == 0 || kRowScaledB)) {
+      // 16-byte-aligned rows: lane l brings the scales of rows (columns) 4l .. 4l+3
+      const float *src = w == 0 ? g.sa + (int64_t)kb * g.M + tl.m0 : g.sb + (int64_t)kb * g.N + tl.n0;
       dma16_s(src, (uint32_t)ln * 16, ls + (w == 0 ? 0 : kBM * 4));
       return;
     }
     if (w == 0) {
-      const float *src = g.sa + (int64_t)kb * g.M + m0;
+      const float *src = g.sa + (int64_t)kb * g.M + tl.m0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, rows_a - 1) * 4, ls + 256 * j);
+      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, tl.rows_a - 1) * 4, ls + 256 * j);
     } else if constexpr (kRowScaledB) {
-      const float *src = g.sb + (int64_t)kb * g.N + n0;
+      const float *src = g.sb + (int64_t)kb * g.N + tl.n0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, tl.rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
     } else {
       // lane l brings sb[n-block nb0 + l][kb] (clamped); lanes 0 and 1 cover
       // the tile's two 128-column blocks
-      const float *src = g.sb + nb0 * g.nk + kb;
+      const int nb0 = tl.n0 / kBK;
+      const int nb_last = (int)((g.N - 1) / kBK) - nb0;
+      const float *src = g.sb + (int64_t)nb0 * g.nk + kb;
       dma4_s(src, (uint32_t)min(ln, nb_last) * (uint32_t)g.nk * 4, ls + kBM * 4);
     }
   };
 
-  auto issue_slice = [&](int kb, int buf) {
+  auto issue_slice = [&](const Tile &tl, int kb, int buf) {
     const int kofs = kb * kBK;
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
-    const uint32_t lb = la + kSliceBytes;
-    if (full_rows && !(ktail && kb == g.nk - 1)) {
-      dma_slice8(a_wave + kofs, b_wave + kofs, voff0, voff1, voff2, voff3, la + w * 4096);
+    const uint8_t *a_tile = g.a + (int64_t)tl.m0 * g.K;
+    const uint8_t *b_tile = g.b + (int64_t)tl.n0 * g.K;
+    if (tl.rows_a == kBM && tl.rows_b == kBN && !(ktail && kb == g.nk - 1)) {
+      dma_slice8(a_tile + (int64_t)(w * 32) * g.K + kofs, b_tile + (int64_t)(w * 32) * g.K + kofs, voff0,
+                 voff1, voff2, voff3, la + w * 4096);
     } else {
       // edge tiles and the ragged last slice: chunks at or past K read a zero page
+      const uint32_t lb = la + kSliceBytes;
       int ln = __lane_id();
       asm volatile("" : "+v"(ln));
       const int rg = ln >> 3;
-      const int k0 = ((ln & 7) ^ rg) * 16;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int grp = w * 4 + j;
         const int r = grp * 8 + rg;
-        const int kc = (j & 1) ? (k0 ^ 16) : k0;
+        const int kc = dma_chunk(ln, j);
         const bool kin = kofs + kc < K;
-        const uint8_t *pa = kin ? a_tile + kofs + (r < rows_a ? (int64_t)r * K : 0) + kc : g_zero16;
-        const uint8_t *pb = kin ? b_tile + kofs + (r < rows_b ? (int64_t)r * K : 0) + kc : g_zero16;
+        const uint8_t *pa = kin ? a_tile + kofs + (r < tl.rows_a ? (int64_t)r * K : 0) + kc : g_zero16;
+        const uint8_t *pb = kin ? b_tile + kofs + (r < tl.rows_b ? (int64_t)r * K : 0) + kc : g_zero16;
         dma16_v(pa, la + grp * 1024);
         dma16_v(pb, lb + grp * 1024);
       }
     }
-    issue_scales(kb, buf);
+    issue_scales(tl, kb, buf);
   };
 
-  // ---- fragment read plan: lane reads row (lane % 16) of each 16-row block,
-  // logical chunks 2q and 2q+1 (q = lane / 16).
+  // ---- fragment read plan: lane reads logical chunks 2q and 2q+1 (q = lane
+  // / 16) of one row per 16-row block: A row fr (= lane % 16) of its m-block.
+  // The MFMAs take the B fragment as their first operand, so each 16x16 result
+  // is (n, m): lane (q, fr) holds output row fr of the m-block at the 4 output
+  // columns of B-fragment rows 4q .. 4q+3.  B-fragment row i of n-block nb is
+  // B row  wn*128 + 32*(nb/2) + 4*(nb%2) + 8*(i/4) + i%4,  so that n-blocks 2p
+  // and 2p+1 give lane (q, fr) the 8 consecutive output columns
+  // wn*128 + 32p + 8q .. +7 (one 16-byte bf16 store).
   const int fr = lane & 15;
   const int q = lane >> 4;
-  const int p0 = (2 * q) ^ lds_swz(fr);
-  const int p1 = p0 ^ 1;
+  // Byte offsets of chunk 2q of a lane's fragment row; chunk 2q+1 is at ^16.
+  // The swizzle of A row wm*64 + 16mb + fr depends on fr and mb%2; that of B
+  // row wn*128 + 32*(nb/2) + 4*(nb%2) + cfr on fr and nb%2.
+  const int cfr = 8 * (fr >> 2) + (fr & 3);                      // B row of fragment row fr, within its group
+  auto swz_a = [&](int t) { return ((fr >> 1) & 1) | (((fr >> 3) & 1) << 1) | ((((fr >> 2) ^ t) & 1) << 2); };
+  auto swz_b = [&](int t) { return ((fr >> 1) & 1) | (((fr >> 2) & 1) << 1) | (((t ^ (fr >> 3)) & 1) << 2); };
+  const uint32_t aoff0 = (uint32_t)(fr * kBK + ((2 * q) ^ swz_a(0)) * 16);
+  const uint32_t aoff1 = (uint32_t)(fr * kBK + ((2 * q) ^ swz_a(1)) * 16);
+  const uint32_t boff0 = (uint32_t)(cfr * kBK + ((2 * q) ^ swz_b(0)) * 16);
+  const uint32_t boff1 = (uint32_t)(cfr * kBK + ((2 * q) ^ swz_b(1)) * 16);
 
   v4f acc[4][8];
 #pragma unroll
@@ -333,62 +311,61 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  auto load_frag = [&](const uint8_t *base, int r) -> v8i {
-    const v4i lo = *reinterpret_cast<const v4i *>(base + r * kBK + p0 * 16);
-    const v4i hi = *reinterpret_cast<const v4i *>(base + r * kBK + p1 * 16);
+  auto frag = [](const uint8_t *row_base, uint32_t off) -> v8i {
+    const v4i lo = *reinterpret_cast<const v4i *>(row_base + off);
+    const v4i hi = *reinterpret_cast<const v4i *>(row_base + (off ^ 16u));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
+  // A fragment of m-block mb, B fragment of n-block nb (compile-time after unrolling)
+  auto load_fragA = [&](const uint8_t *base, int mb) -> v8i {
+    return frag(base + (wm * 64 + mb * 16) * kBK, (mb & 1) ? aoff1 : aoff0);
+  };
+  auto load_fragB = [&](const uint8_t *base, int nb) -> v8i {
+    return frag(base + (wn * 128 + 32 * (nb >> 1) + 4 * (nb & 1)) * kBK, (nb & 1) ? boff1 : boff0);
+  };
+  // first B-fragment column of n-block nb seen by lane (q, fr), relative to the wave's 128
+  auto colB = [&](int nb) { return 32 * (nb >> 1) + 4 * (nb & 1) + 8 * q; };
 
-  // ---- K loop.  Slice kb is computed from buffer (kb - kb_begin) & 1 while
-  // slice kb+1 is copied into the other one.  The barrier that publishes slice
-  // kb+1 sits before the last n-block step of slice kb, so that the reads of
-  // slice kb+1's A fragments, first B fragment and scales overlap the MFMAs of
+  // ---- K loop.  Slice s of the stream is computed from buffer s & 1 while
+  // slice s+1 is copied into the other one.  The barrier that publishes slice
+  // s+1 sits before the last n-block step of slice s, so that the reads of
+  // slice s+1's A fragments, first B fragment and scales overlap the MFMAs of
   // that step instead of stalling every wave at the start of the slice.
   v8i af[4];                 // A fragments of the wave's 4 m-blocks
   v8i bf[2];                 // B fragments of n-blocks nb (in use) and nb+1 (landing)
-  v4f sa[4];                 // row scales sA of the lane's 4 rows in each m-block
-  float sbn0 = 1.0f;         // row-scaled B: column scale of the coming slice's n-block 0
+  float sa[4];               // row scale sA of the lane's row in each m-block
+  v4f sbn0 = {1.f, 1.f, 1.f, 1.f};   // row-scaled B: column scales of the coming slice's n-block 0
   float sbk = 1.0f;          // block-scaled B: the coming slice's scale of the wave's 128 columns
   auto load_scales = [&](int buf) {
     const float *lsa = sscale[buf][0];
     const float *lsb = sscale[buf][1];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) sa[mb] = *reinterpret_cast<const v4f *>(&lsa[wm * 64 + mb * 16 + 4 * q]);
-    if constexpr (kRowScaledB) sbn0 = lsb[wn * 128 + fr];
+    for (int mb = 0; mb < 4; ++mb) sa[mb] = lsa[wm * 64 + mb * 16 + fr];
+    if constexpr (kRowScaledB) sbn0 = *reinterpret_cast<const v4f *>(&lsb[wn * 128 + colB(0)]);
     else sbk = lsb[wn];
   };
 
-  if (kb_begin < kb_end) {
-    issue_slice(kb_begin, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    bf[0] = load_frag(smem[0][1], wn * 128 + fr);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) af[mb] = load_frag(smem[0][0], wm * 64 + mb * 16 + fr);
-    load_scales(0);
-  }
-
-  // One slice.  Step nb issues the 4 MFMAs of n-block nb; the partial of
-  // n-block nb-1 is promoted into the accumulators from P[mb] right before
-  // MFMA (nb, mb) overwrites it, and the B fragment of n-block nb+1 is read
-  // one step ahead.  kNext: a slice follows in this work item.
-  auto slice = [&](int kb, auto next_c) {
-    constexpr bool kNext = decltype(next_c)::value;
-    const int buf = (kb - kb_begin) & 1;
+  // One slice from buffer `buf`.  Step nb issues the 4 MFMAs of n-block nb;
+  // the partial of n-block nb-1 is promoted into the accumulators from P[mb]
+  // right before MFMA (nb, mb) overwrites it, and the B fragment of n-block
+  // nb+1 is read one step ahead.  kNext: slice kb_next of item `nxt` follows.
+  auto slice = [&](int buf, const Tile &nxt, int kb_next, auto next_c, auto preload_c) {
+    constexpr bool kNext = decltype(next_c)::value;           // a slice follows: copy it now
+    constexpr bool kPre = kNext && decltype(preload_c)::value; // read its fragments in the last step
     const uint8_t *Bs = smem[buf][1];
     const float *lsb = sscale[buf][1];
     v4f P[4];
-    float sbv[8];              // row-scaled B: column scale of each n-block
+    v4f sbv[8];                // row-scaled B: column scales of each n-block
     sbv[0] = sbn0;
-    v4f sc[4];                 // block-scaled B: promotion factors sA * sB
-    // the buffer of slice kb-1 was released by the barrier inside slice kb-1
-    if constexpr (kNext) issue_slice(kb + 1, buf ^ 1);
+    float sc[4];               // block-scaled B: promotion factors sA * sB
+    // the buffer of the previous slice was released by the barrier inside it
+    if constexpr (kNext) issue_slice(nxt, kb_next, buf ^ 1);
     auto promote = [&](int pb, int mb) {
       if constexpr (kRowScaledB) {
         const v4f ps = P[mb] * sbv[pb];                          // column scale first, in place
-        acc[mb][pb] = __builtin_elementwise_fma(ps, sa[mb], acc[mb][pb]);
+        acc[mb][pb] = __builtin_elementwise_fma(ps, (v4f)sa[mb], acc[mb][pb]);
       } else {
-        acc[mb][pb] = __builtin_elementwise_fma(P[mb], sc[mb], acc[mb][pb]);
+        acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)sc[mb], acc[mb][pb]);
       }
     };
 #pragma unroll
@@ -396,21 +373,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       if (nb == 7) {
         // Every wave holds its n-block 7 fragment (lgkmcnt) and has landed its
-        // share of slice kb+1 (vmcnt): past the barrier slice kb+1 is readable
-        // and nothing reads slice kb's buffer any more.
+        // share of the next slice (vmcnt): past the barrier the next slice is
+        // readable and nothing reads this slice's buffer any more.
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kRowScaledB && nb + 1 < 8) sbv[nb + 1] = lsb[wn * 128 + (nb + 1) * 16 + fr];
-      if (nb + 1 < 8) bf[(nb + 1) & 1] = load_frag(Bs, wn * 128 + (nb + 1) * 16 + fr);
-      if (nb == 7 && kNext) bf[0] = load_frag(smem[buf ^ 1][1], wn * 128 + fr);
+      if (kRowScaledB && nb + 1 < 8) sbv[nb + 1] = *reinterpret_cast<const v4f *>(&lsb[wn * 128 + colB(nb + 1)]);
+      if (nb + 1 < 8) bf[(nb + 1) & 1] = load_fragB(Bs, nb + 1);
+      if (nb == 7 && kPre) bf[0] = load_fragB(smem[buf ^ 1][1], 0);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (nb > 0) promote(nb - 1, mb);
         P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            af[mb], bf[nb & 1], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        if (nb == 7 && kNext) af[mb] = load_frag(smem[buf ^ 1][0], wm * 64 + mb * 16 + fr);
+            bf[nb & 1], af[mb], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+        if (nb == 7 && kPre) af[mb] = load_fragA(smem[buf ^ 1][0], mb);
         if (nb == 0 && !kRowScaledB) sc[mb] = sa[mb] * sbk;
       }
       // issue order within the step: LDS reads first (a whole step to land),
@@ -422,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-          if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+          if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
         }
       } else if (nb < 7) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);
@@ -432,38 +409,130 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       } else {
-        if (kNext) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (kNext) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) promote(7, mb);
-    if constexpr (kNext) load_scales(buf ^ 1);
+    if constexpr (kPre) load_scales(buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  {
-    int kb = kb_begin;
-    for (; kb + 1 < kb_end; ++kb) slice(kb, std::true_type{});
-    if (kb < kb_end) slice(kb, std::false_type{});
-  }
+  // Output of one item straight from the accumulators: lane (q, fr) holds,
+  // for m-block mb and n-block pair p, row m0 + wm*64 + 16mb + fr at the 8
+  // columns n0 + wn*128 + 32p + 8q .. +7 (n-block 2p: the first 4, 2p+1: the
+  // last 4): one 16-byte store of bf16, two of fp32.  Then the accumulators
+  // are cleared for the next item.
+  auto store_item = [&](const Tile &tl) {
+    const int64_t wbase = (int64_t)(tl.m0 + wm * 64) * g.N + tl.n0 + wn * 128;
+    const int64_t loff = (int64_t)fr * g.N + 8 * q;
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    auto pk = [](v4f v, int h) -> uint32_t {
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(h ? __builtin_shufflevector(v, v, 2, 3)
+                                                                    : __builtin_shufflevector(v, v, 0, 1), v2bf));
+    };
+    if constexpr (kBf16Out && !kToWs) {
+      const bool fast = tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 7) == 0;
+      if (fast) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const v4f a0 = acc[mb][2 * pp], a1 = acc[mb][2 * pp + 1];
+            *reinterpret_cast<u32x4 *>(ob + loff + 32 * pp) = (u32x4){pk(a0, 0), pk(a0, 1), pk(a1, 0), pk(a1, 1)};
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+          if (m >= g.M) continue;
+          uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int n = tl.n0 + wn * 128 + colB(nb);
+            const uint32_t lo = pk(acc[mb][nb], 0), hi = pk(acc[mb][nb], 1);
+            const uint16_t h[4] = {(uint16_t)(lo & 0xffffu), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xffffu),
+                                   (uint16_t)(hi >> 16)};
+            uint16_t *d = ob + (int64_t)fr * g.N + colB(nb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) d[e] = h[e];
+          }
+        }
+      }
+    } else {
+      float *o = (kToWs ? g.ws + (int64_t)tl.split * g.M * g.N : reinterpret_cast<float *>(g.out)) + wbase;
+      const bool fast = tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0;
+      if (fast) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          float *ob = o + (int64_t)(mb * 16) * g.N;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            *reinterpret_cast<v4f *>(ob + loff + 32 * pp) = acc[mb][2 * pp];
+            *reinterpret_cast<v4f *>(ob + loff + 32 * pp + 4) = acc[mb][2 * pp + 1];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+          if (m >= g.M) continue;
+          float *ob = o + (int64_t)(mb * 16) * g.N;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const int n = tl.n0 + wn * 128 + colB(nb);
+            float *d = ob + (int64_t)fr * g.N + colB(nb);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < g.N) d[e] = acc[mb][nb][e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+  };
 
-  // ---- epilogue.  Lane holds rows wm*64 + mb*16 + 4q + e, columns
-  // wn*128 + nb*16 + fr of the tile.  The tile is staged through the (now
-  // idle) LDS in row-major order and leaves as 16-byte row chunks: bf16 in two
-  // passes of 128 rows, fp32 in four passes of 64 rows.
-  if constexpr (kToWs) {
-    store_tile<float>(acc, g.ws + (int64_t)split * g.M * g.N, g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
-  } else if constexpr (kBf16Out) {
-    store_tile<uint16_t>(acc, reinterpret_cast<uint16_t *>(g.out), g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
-  } else {
-    store_tile<float>(acc, reinterpret_cast<float *>(g.out), g, m0, n0, &smem[0][0][0], wm, wn, q, fr);
+  Tile cur = tile_of(g, item);
+  issue_slice(cur, cur.kb_begin, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  bf[0] = load_fragB(smem[0][1], 0);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) af[mb] = load_fragA(smem[0][0], mb);
+  load_scales(0);
+
+  int buf = 0;
+  for (;;) {
+    for (int kb = cur.kb_begin; kb + 1 < cur.kb_end; ++kb) {
+      slice(buf, cur, kb + 1, std::true_type{}, std::true_type{});
+      buf ^= 1;
+    }
+    // Last slice of the item: the first slice of the next item is copied and
+    // its fragments read meanwhile.  After the last item this re-reads the
+    // item's own first slice, which keeps a single code path (a separate
+    // final-slice variant costs the register allocator its accumulators).
+    const int next_item = item + (int)gridDim.x;
+    const bool more = next_item < total_items;
+    const Tile nxt = tile_of(g, more ? next_item : item);
+    slice(buf, nxt, nxt.kb_begin, std::true_type{}, std::true_type{});
+    buf ^= 1;
+    store_item(cur);
+    if (!more) break;
+    item = next_item;
+    cur = nxt;
   }
 }
 
@@ -529,6 +598,20 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// Compute units of the current device (one persistent workgroup each),
+// queried once per device.
+static int compute_units() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                     void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream) {
@@ -546,7 +629,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   g.M = M; g.N = N; g.K = K;
   g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
   g.splits = p.splits; g.spl = p.spl;
-  const dim3 grid((unsigned)((int64_t)p.tiles_m * p.tiles_n * p.splits));
+  const dim3 grid((unsigned)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n * p.splits, compute_units()));
   const bool row_b = mode == 2;
   const bool to_ws = p.splits > 1;
 #define PURO_LAUNCH(RB, BF, WS) \
