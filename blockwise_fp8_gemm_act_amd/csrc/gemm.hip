@@ -349,9 +349,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // the partial of n-block nb-1 is promoted into the accumulators from P[mb]
   // right before MFMA (nb, mb) overwrites it, and the B fragment of n-block
   // nb+1 is read one step ahead.  kNext: slice kb_next of item `nxt` follows.
-  auto slice = [&](int buf, const Tile &nxt, int kb_next, auto next_c, auto preload_c) {
+  auto slice = [&](int buf, const Tile &nxt, int kb_next, auto next_c, auto preload_c, auto first_c) {
     constexpr bool kNext = decltype(next_c)::value;           // a slice follows: copy it now
     constexpr bool kPre = kNext && decltype(preload_c)::value; // read its fragments in the last step
+    constexpr bool kFirst = decltype(first_c)::value;          // first slice of an item: accumulators start at 0
     const uint8_t *Bs = smem[buf][1];
     const float *lsb = sscale[buf][1];
     v4f P[4];
@@ -361,11 +362,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     // the buffer of the previous slice was released by the barrier inside it
     if constexpr (kNext) issue_slice(nxt, kb_next, buf ^ 1);
     auto promote = [&](int pb, int mb) {
+      const v4f prev = kFirst ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[mb][pb];
       if constexpr (kRowScaledB) {
         const v4f ps = P[mb] * sbv[pb];                          // column scale first, in place
-        acc[mb][pb] = __builtin_elementwise_fma(ps, (v4f)sa[mb], acc[mb][pb]);
+        acc[mb][pb] = __builtin_elementwise_fma(ps, (v4f)sa[mb], prev);
       } else {
-        acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)sc[mb], acc[mb][pb]);
+        acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)sc[mb], prev);
       }
     };
 #pragma unroll
@@ -428,8 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // Output of one item straight from the accumulators: lane (q, fr) holds,
   // for m-block mb and n-block pair p, row m0 + wm*64 + 16mb + fr at the 8
   // columns n0 + wn*128 + 32p + 8q .. +7 (n-block 2p: the first 4, 2p+1: the
-  // last 4): one 16-byte store of bf16, two of fp32.  Then the accumulators
-  // are cleared for the next item.
+  // last 4): one 16-byte store of bf16, two of fp32.
   auto store_item = [&](const Tile &tl) {
     const int64_t wbase = (int64_t)(tl.m0 + wm * 64) * g.N + tl.n0 + wn * 128;
     const int64_t loff = (int64_t)fr * g.N + 8 * q;
@@ -499,10 +500,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         }
       }
     }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
   };
 
   Tile cur = tile_of(g, item);
@@ -516,8 +513,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 
   int buf = 0;
   for (;;) {
-    for (int kb = cur.kb_begin; kb + 1 < cur.kb_end; ++kb) {
-      slice(buf, cur, kb + 1, std::true_type{}, std::true_type{});
+    // The first slice of an item writes the accumulators instead of adding to
+    // them; an item of one slice starts from cleared accumulators instead.
+    if (cur.kb_end - cur.kb_begin > 1) {
+      slice(buf, cur, cur.kb_begin + 1, std::true_type{}, std::true_type{}, std::true_type{});
+      buf ^= 1;
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int kb = cur.kb_begin + 1; kb + 1 < cur.kb_end; ++kb) {
+      slice(buf, cur, kb + 1, std::true_type{}, std::true_type{}, std::false_type{});
       buf ^= 1;
     }
     // Last slice of the item: the first slice of the next item is copied and
@@ -527,7 +535,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const int next_item = item + (int)gridDim.x;
     const bool more = next_item < total_items;
     const Tile nxt = tile_of(g, more ? next_item : item);
-    slice(buf, nxt, nxt.kb_begin, std::true_type{}, std::true_type{});
+    slice(buf, nxt, nxt.kb_begin, std::true_type{}, std::true_type{}, std::false_type{});
     buf ^= 1;
     store_item(cur);
     if (!more) break;
