@@ -33,8 +33,11 @@
 //    bank-conflict free;
 //  - rows past M or N are read from clamped (valid) rows and never stored;
 //    K chunks past K read a 16-byte zero page, so a ragged last slice adds 0;
-//  - optional split-K writes fp32 partials to a workspace that a second
-//    kernel sums in a fixed order (deterministic).
+//  - an item's slices are promoted in a fixed order that depends on the item
+//    alone (a rotation by (item % 8) / 8 of its K range, which keeps the
+//    items that share an XCD's L2 in lockstep and staggers the 8 XCDs);
+//    optional split-K writes fp32 partials to a workspace that a second
+//    kernel sums in a fixed order.  Results are deterministic.
 #include "device_common.h"
 #include "launch.h"
 
@@ -159,6 +162,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 struct Tile {
   int m0, n0;                // first row of A / of B (M, N < 2^31)
   int kb_begin, kb_end;
+  int rot;                   // the item's slices run kb_begin + rot, ..., kb_end - 1, kb_begin, ...
   int rows_a, rows_b;        // valid rows of A / B in the tile
   int split;
 };
@@ -174,9 +178,22 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item) {
   t.n0 = tn * kBN;
   t.kb_begin = t.split * g.spl;
   t.kb_end = min(g.nk, t.kb_begin + g.spl);
+  // Items that run on one XCD at the same time (item = b + rG, workgroup b on
+  // XCD b % 8, G a multiple of 8) share item % 8 and so walk K in lockstep,
+  // sharing their A and B panels through that XCD's L2; the 8 XCDs start
+  // 1/8 of the K range apart.  The order depends on the item alone.
+  t.rot = (int)(((unsigned)(item & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
   t.rows_a = min((int)g.M - t.m0, kBM);
   t.rows_b = min((int)g.N - t.n0, kBN);
   return t;
+}
+
+// K slice of step i (0 .. kb_end - kb_begin - 1) of an item.
+__device__ __forceinline__ int kb_at(const Tile &t, int i) {
+  int k = t.rot + i;
+  const int n = t.kb_end - t.kb_begin;
+  if (k >= n) k -= n;
+  return t.kb_begin + k;
 }
 
 // Persistent kernel: workgroup b computes work items b, b + G, b + 2G, ...
@@ -503,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   };
 
   Tile cur = tile_of(g, item);
-  issue_slice(cur, cur.kb_begin, 0);
+  issue_slice(cur, kb_at(cur, 0), 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   bf[0] = load_fragB(smem[0][1], 0);
@@ -516,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     // The first slice of an item writes the accumulators instead of adding to
     // them; an item of one slice starts from cleared accumulators instead.
     if (cur.kb_end - cur.kb_begin > 1) {
-      slice(buf, cur, cur.kb_begin + 1, std::true_type{}, std::true_type{}, std::true_type{});
+      slice(buf, cur, kb_at(cur, 1), std::true_type{}, std::true_type{}, std::true_type{});
       buf ^= 1;
     } else {
 #pragma unroll
@@ -524,8 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
-    for (int kb = cur.kb_begin + 1; kb + 1 < cur.kb_end; ++kb) {
-      slice(buf, cur, kb + 1, std::true_type{}, std::true_type{}, std::false_type{});
+    for (int i = 1; i + 1 < cur.kb_end - cur.kb_begin; ++i) {
+      slice(buf, cur, kb_at(cur, i + 1), std::true_type{}, std::true_type{}, std::false_type{});
       buf ^= 1;
     }
     // Last slice of the item: the first slice of the next item is copied and
@@ -535,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const int next_item = item + (int)gridDim.x;
     const bool more = next_item < total_items;
     const Tile nxt = tile_of(g, more ? next_item : item);
-    slice(buf, nxt, nxt.kb_begin, std::true_type{}, std::true_type{}, std::false_type{});
+    slice(buf, nxt, kb_at(nxt, 0), std::true_type{}, std::true_type{}, std::false_type{});
     buf ^= 1;
     store_item(cur);
     if (!more) break;

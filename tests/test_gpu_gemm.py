@@ -98,6 +98,18 @@ def test_split_k_path(orc, mode):
         check_full(orc, mode, a, sa, b, sb, dtype, "split-K mode %d" % mode)
 
 
+@pytest.mark.parametrize("mode,M,N,K", [(FPROP, 8192, 2600, 2048), (WGRAD, 1024, 768, 8192), (DGRAD, 768, 1280, 1040)])
+def test_repeated_calls_bitwise_identical(orc, mode, M, N, K):
+    """The slice order and split-K sums are fixed: two calls give the same bits (several work items per
+    workgroup, a split-K shape, edge tiles and a ragged K)."""
+    a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=M + N + K)
+    for dtype in (torch.float32, torch.bfloat16):
+        r1 = run_gpu(mode, a, sa, b, sb, dtype)
+        r2 = run_gpu(mode, a, sa, b, sb, dtype)
+        iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(r1.view(iv), r2.view(iv)), "mode %d %dx%dx%d %s" % (mode, M, N, K, dtype)
+
+
 def test_zero_k_writes_zeros():
     for dtype in (torch.float32, torch.bfloat16):
         a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
