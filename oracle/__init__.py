@@ -68,6 +68,7 @@ def _load():
     for name in ("orc_quant_act_1x128", "orc_quant_w_128x128",
                  "orc_quant_act_128x1_t", "orc_quant_w_128x128_t"):
         getattr(lib, name).argtypes = [P, I64, I64, P, P]
+    lib.orc_requant_act_t.argtypes = [P, P, I64, I64, P, P]
     lib.orc_gemm_element.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, I64, I64]
     lib.orc_gemm_element.restype = ctypes.c_double
     lib.orc_gemm.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, P]
@@ -186,6 +187,21 @@ def quant_w_128x128_t(w: np.ndarray):
     qt = np.empty((C, R), dtype=np.uint8)
     st = np.empty((_cdiv(C, TILE), _cdiv(R, TILE)), dtype=np.float32)
     _load().orc_quant_w_128x128_t(_ptr(w), R, C, _ptr(qt), _ptr(st))
+    return qt, st
+
+
+def requant_act_t(q: np.ndarray, s: np.ndarray):
+    """Saved 1x128 codes q uint8 [R][C] with scales s float32 [ceil(C/128)][R]
+    -> (qt uint8 [C][R], st float32 [ceil(R/128)][C]): dequantize to fp32, then
+    quantize in transposed 128x1 tiles."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    R, C = q.shape
+    if s.shape != (_cdiv(C, TILE), R):
+        raise ValueError("scales must be [ceil(C/128)][R], got %s" % (s.shape,))
+    qt = np.empty((C, R), dtype=np.uint8)
+    st = np.empty((_cdiv(R, TILE), C), dtype=np.float32)
+    _load().orc_requant_act_t(_ptr(q), _ptr(s), R, C, _ptr(qt), _ptr(st))
     return qt, st
 
 

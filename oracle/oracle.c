@@ -256,6 +256,48 @@ void orc_quant_w_128x128_t(const uint16_t *w, int64_t R, int64_t C,
     }
 }
 
+/* Requantize saved 1x128 activation codes into transposed 128x1 tiles (the
+ * other reading of the backward's "transpose-requantize": the forward pass
+ * keeps only the FP8 codes of an activation, and the wgrad operand is rebuilt
+ * from them).  Two steps, applied literally:
+ *   1. dequantize to fp32: d[r][c] = fp32(dec(q[r][c]) * s[c/128][r]) (the
+ *      product is formed exactly and rounded once to fp32);
+ *   2. quantize d with the 128x1 rule of orc_quant_act_128x1_t: per tile of
+ *      128 rows of one column, st = amax/448 (1 if the tile is all zero) and
+ *      qt = e4m3(fp32(d / st)).
+ * q: uint8 [R][C] with scales s: fp32 [ceil(C/128)][R] (the output layout of
+ * orc_quant_act_1x128).  qt: uint8 [C][R], qt[c][r] the new code of element
+ * (r, c); st: fp32 [ceil(R/128)][C].  NaN codes (0x7F, 0xFF) are outside the
+ * contract; the quantizers never emit them. */
+static float deq_act_f32(uint8_t c, float s)
+{
+    return (float)(orc_e4m3_decode(c) * (double)s);
+}
+
+void orc_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C,
+                       uint8_t *qt, float *st)
+{
+    int64_t ni = ceil_div(R, TILE);
+    int64_t c;
+#pragma omp parallel for schedule(static)
+    for (c = 0; c < C; ++c) {
+        int64_t i, j = c / TILE;
+        for (i = 0; i < ni; ++i) {
+            int64_t r0 = i * TILE, r1 = r0 + TILE < R ? r0 + TILE : R, r;
+            float amax = 0.0f, sc;
+            for (r = r0; r < r1; ++r) {
+                float v = fabsf(deq_act_f32(q[r * C + c], s[j * R + r]));
+                if (v > amax)
+                    amax = v;
+            }
+            sc = orc_tile_scale(amax);
+            st[i * C + c] = sc;
+            for (r = r0; r < r1; ++r)
+                qt[c * R + r] = orc_quantize_value(deq_act_f32(q[r * C + c], s[j * R + r]), sc);
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* GEMM                                                                */
 /* ------------------------------------------------------------------ */

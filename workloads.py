@@ -155,3 +155,20 @@ def random_bf16(shape, seed: int, std: float = 1.0, device="cpu") -> torch.Tenso
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return (torch.randn(shape, generator=g, device=device) * std).to(torch.bfloat16)
+
+
+def random_codes(shape, seed: int) -> np.ndarray:
+    """Uniformly drawn finite e4m3 code bytes (every byte except 0x7F and 0xFF)."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    c = torch.randint(0, 254, shape, generator=g, dtype=torch.int64).numpy()
+    c = c + (c >= 0x7F)                      # skip 0x7F; 0xFF is above the drawn range
+    return c.astype(np.uint8)
+
+
+def random_scales(shape, seed: int, log2_lo: float = -20.0, log2_hi: float = 4.0) -> np.ndarray:
+    """Positive fp32 scales, log-uniform in [2^log2_lo, 2^log2_hi)."""
+    g = torch.Generator()
+    g.manual_seed(seed)
+    e = torch.rand(shape, generator=g, dtype=torch.float64) * (log2_hi - log2_lo) + log2_lo
+    return torch.exp2(e).to(torch.float32).numpy()
