@@ -7,11 +7,11 @@ device memory and streams.  There is no fallback: if the library is missing,
 importing this package fails.
 
 The raw C calls keep their C names (``puro_quant_act_1x128``,
-``puro_quant_w_128x128``, ``puro_quant_transpose``,
+``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_requant_act_t``,
 ``puro_gemm_fp8_blockwise``, ...) and take integer device pointers.  The
 tensor-level helpers ``quant_act_1x128``, ``quant_w_128x128``,
-``quant_transpose``, ``gemm_fp8_blockwise`` allocate outputs with torch and
-call them on the current stream.
+``quant_transpose``, ``requant_act_t``, ``gemm_fp8_blockwise`` allocate
+outputs with torch and call them on the current stream.
 """
 from __future__ import annotations
 
@@ -33,7 +33,7 @@ T_ACT, T_WEIGHT = 0, 1
 TILE = 128
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libpuro.so is not built: run `python -m blockwise_fp8_gemm_act_amd.build` "
+    raise ImportError("libpuro.so is not built: run `python blockwise_fp8_gemm_act_amd/build.py` "
                       "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -45,6 +45,8 @@ _lib.puro_quant_w_128x128.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.puro_quant_w_128x128.restype = ctypes.c_int
 _lib.puro_quant_transpose.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.puro_quant_transpose.restype = ctypes.c_int
+_lib.puro_requant_act_t.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
+_lib.puro_requant_act_t.restype = ctypes.c_int
 _lib.puro_gemm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64]
 _lib.puro_gemm_workspace_bytes.restype = ctypes.c_size_t
 _lib.puro_gemm_fp8_blockwise.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
@@ -74,6 +76,10 @@ def puro_quant_w_128x128(w, rows, cols, q, s, stream=None) -> int:
 
 def puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream=None) -> int:
     return _lib.puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream)
+
+
+def puro_requant_act_t(q, s, rows, cols, qt, st, stream=None) -> int:
+    return _lib.puro_requant_act_t(q, s, rows, cols, qt, st, stream)
 
 
 def puro_gemm_workspace_bytes(mode, M, N, K) -> int:
@@ -163,6 +169,21 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
                                 q.data_ptr() if dual else None, s.data_ptr() if dual else None,
                                 _stream(stream)), "puro_quant_transpose")
     return (qt, st, q, s) if dual else (qt, st)
+
+
+def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=None):
+    """Saved 1x128 codes q uint8 [R][C] and scales s fp32 [ceil(C/128)][R] ->
+    (qt uint8 [C][R], st fp32 [ceil(R/128)][C]) in transposed 128x1 tiles."""
+    if q.dtype != torch.uint8 or q.dim() != 2 or not q.is_cuda or not q.is_contiguous():
+        raise TypeError("q must be a contiguous 2-D uint8 CUDA tensor")
+    R, C = q.shape
+    if s.dtype != torch.float32 or tuple(s.shape) != (_cdiv(C, TILE), R) or not s.is_contiguous():
+        raise ValueError("s must be a contiguous fp32 tensor of shape [ceil(C/128)][R]")
+    qt = torch.empty((C, R), dtype=torch.uint8, device=q.device) if qt is None else qt
+    st = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device) if st is None else st
+    _check(puro_requant_act_t(q.data_ptr(), s.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
+                              _stream(stream)), "puro_requant_act_t")
+    return qt, st
 
 
 def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):

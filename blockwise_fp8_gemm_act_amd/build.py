@@ -1,6 +1,7 @@
 """Build libpuro.so (the gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-Usage: python -m blockwise_fp8_gemm_act_amd.build
+Usage: python blockwise_fp8_gemm_act_amd/build.py  (run as a script: importing the
+package would bind the symbols of a stale library before it is rebuilt)
 """
 from __future__ import annotations
 

@@ -160,6 +160,19 @@ puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t ro
   return launched(puro::run_quant_t_w(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
 }
 
+puro_status puro_requant_act_t(const uint8_t *q, const float *s, int64_t rows, int64_t cols,
+                               uint8_t *qt, float *st, puro_stream_t stream) {
+  if (!shape_ok(rows, cols) || cols % 16 != 0 || rows % 16 != 0) return PURO_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return PURO_OK;
+  if (!q || !s || !qt || !st) return PURO_ERR_NULL;
+  if (!aligned16(q) || !aligned16(s) || !aligned16(qt) || !aligned16(st)) return PURO_ERR_ALIGN;
+  const Range in[] = {rng(q, rows * cols), rng(s, cdiv(cols, 128) * rows * 4)};
+  const Range out[] = {rng(qt, rows * cols), rng(st, cdiv(rows, 128) * cols * 4)};
+  if (any_alias(in, 2, out, 2)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_requant_act_t(q, s, rows, cols, qt, st, (hipStream_t)stream));
+}
+
 size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int64_t K) {
   if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return 0;

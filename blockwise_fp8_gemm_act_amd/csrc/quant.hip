@@ -34,6 +34,40 @@ struct QuantArgs {
   float *st;               // scales of the transposed codes
 };
 
+// Transposed codes of one 128x128 block, staged in LDS, to global memory.
+// LDS row c (a column of the block, an output row) holds 16 slots of 8 codes
+// (8 input rows each); logical slot g is stored at physical slot g ^ (c / 8),
+// so that the 8-byte slot writes of 16 consecutive column groups and the
+// 16-byte chunk reads below are both free of bank conflicts.  Each of the 256
+// threads writes four 16-byte chunks; a run of 8 threads covers one 128-byte
+// output row segment.
+__device__ __forceinline__ void put_transposed_slot(uint8_t *lds_t, int lc, int g, u32x2 codes) {
+  *reinterpret_cast<u32x2 *>(&lds_t[lc * kTile + ((g ^ (lc >> 3)) * 8)]) = codes;
+}
+
+template <bool kNtStore>
+__device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *qt, int64_t R, int64_t C,
+                                                 int64_t bi, int64_t bj, int t) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int chunk = t + 256 * u;
+    const int lc = chunk >> 3;          // block column = output row
+    const int p = chunk & 7;            // physical 16-byte chunk in the LDS row
+    const int xs = (lc >> 3) & 15;      // swizzle of this LDS row
+    u32x4 d = *reinterpret_cast<const u32x4 *>(&lds_t[lc * kTile + p * 16]);
+    if (xs & 1) d = (u32x4){d.z, d.w, d.x, d.y};
+    const int l = p ^ (xs >> 1);        // logical 16-byte chunk = rows 16l .. 16l+15
+    const int64_t orow = bj * kTile + lc;
+    const int64_t ocol = bi * kTile + l * 16;
+    if (orow < C && ocol < R) {
+      if constexpr (kNtStore)
+        __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(qt + orow * R + ocol));
+      else
+        *reinterpret_cast<u32x4 *>(qt + orow * R + ocol) = d;
+    }
+  }
+}
+
 // kRow:   1x128 scales (per row of the block)       -> row-major output
 // kCol:   128x1 scales (per column of the block)    -> transposed output
 // kBlock: one 128x128 scale                         -> row-major and/or transposed output
@@ -213,8 +247,6 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) fast &= cs[c] >= kFastDivMinScale;
     refresh();
-    // LDS row c (a column of the block) holds 16 slots of 8 codes (8 rows);
-    // slot rg is stored at physical slot rg ^ (c / 8).
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[8];
@@ -229,25 +261,167 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
       u32x2 col;
       col.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
       col.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
-      const int lc = cc * 8 + c;
-      *reinterpret_cast<u32x2 *>(&lds_t[lc * kTile + ((rg ^ cc) * 8)]) = col;
+      put_transposed_slot(lds_t, cc * 8 + c, rg, col);
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int chunk = t + 256 * u;
-      const int lc = chunk >> 3;          // block column = output row
-      const int p = chunk & 7;            // physical 16-byte chunk in the LDS row
-      const int xs = (lc >> 3) & 15;      // swizzle of this LDS row
-      u32x4 d = *reinterpret_cast<const u32x4 *>(&lds_t[lc * kTile + p * 16]);
-      if (xs & 1) d = (u32x4){d.z, d.w, d.x, d.y};
-      const int l = p ^ (xs >> 1);        // logical 16-byte chunk = rows 16l .. 16l+15
-      const int64_t orow = bj * kTile + lc;
-      const int64_t ocol = bi * kTile + l * 16;
-      if (orow < a.C && ocol < a.R)
-        __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(a.qt + orow * a.R + ocol));
-    }
+    flush_transposed<true>(lds_t, a.qt, a.R, a.C, bi, bj, t);
   }
+}
+
+// Requantization of saved 1x128 activation codes into transposed 128x1 tiles:
+// each code is dequantized to fp32 with its row tile's scale (one IEEE
+// multiply, so the exact product rounded once), then quantized again with
+// the 128x1 rule: per column of the block, st = amax/448 and
+// qt = e4m3(fp32(d / st)).
+//
+// Division.  d is an arbitrary fp32 value here, not a bf16 one, so the
+// one-step reciprocal of the bf16 kernels is not used.  For a column scale b
+// in [2^-60, 2^60] the quotient is formed from a two-word reciprocal
+// rh + rl = 1/b (rh the rounded reciprocal, rl the rounded residual times
+// rh): y = fma(d, rh, d * rl) is then a faithful quotient, and one residual
+// correction z = fma(fma(-y, b, d), rh, y) (Markstein) rounds it correctly.
+// No step underflows while |d / b| >= 2^-12; below that both z and the true
+// quotient lie under 2^-10 and take the zero code of d's sign.  A thread with
+// a column scale outside that range uses the IEEE division.  Five operations per
+// element instead of the IEEE division's dozen, which left the kernel bound
+// by the vector ALU rather than by memory.
+//
+// One workgroup of 256 threads owns one 128x128 block of the code matrix.
+// Within a block all 128 columns belong to one 1x128 tile column, so each row
+// has a single input scale.  Thread t owns 8 rows (rg = t/16) x 8 columns
+// (cc = t%16): 8-byte code loads, so the 16 lanes of a DPP row read one
+// 128-byte row segment, and two 16-byte loads of its 8 row scales.  Rows and
+// columns are multiples of 16, so a thread's 8 rows and 8 columns are either
+// all inside the matrix or all outside it.
+//
+// Memory order.  Consecutive workgroups walk down a block column (block row
+// index fastest), so the blocks in flight together write adjacent 128-byte
+// segments of the same output rows; loads and stores are ordinary cached
+// accesses.  Measured on MI355X for a 16384 x 6144 input, the same transposed
+// byte movement ran 31 us this way against 46 us with workgroups walking
+// along block rows and non-temporal accesses (a plain 100 MB device copy of
+// the same bytes: 28 us).  The partial column maxima share the LDS buffer of
+// the transposed codes (they are dead before the codes are staged), which
+// leaves room for more resident workgroups.
+struct RequantArgs {
+  const uint8_t *q;        // saved codes [R][C]
+  const float *s;          // their 1x128 scales [nj][R]
+  int64_t R, C;
+  int64_t ni, nj;
+  uint8_t *qt;             // transposed codes [C][R]
+  float *st;               // 128x1 scales [ni][C]
+};
+
+constexpr float kRequantFastMin = 0x1p-60f;
+constexpr float kRequantFastMax = 0x1p60f;
+
+// fp32(d / b) from b, rh = fp32(1/b) and rl = fp32((1 - b*rh) * rh); exact
+// (see above) for b in [kRequantFastMin, kRequantFastMax] and |d/b| >= 2^-12.
+__device__ __forceinline__ float quot_2w(float d, float b, float rh, float rl) {
+  const float y = __builtin_fmaf(d, rh, d * rl);
+  const float e = __builtin_fmaf(-y, b, d);
+  const float z = __builtin_fmaf(e, rh, y);
+  return __builtin_copysignf(z, d);
+}
+
+__global__ __launch_bounds__(256) void requant_t_kernel(RequantArgs a) {
+  __shared__ __align__(16) uint8_t lds_t[kTile * kTile];  // transposed codes; first the partial maxima
+  __shared__ __align__(16) float lds_cols[kTile];        // column scales b
+  __shared__ __align__(16) float lds_colh[kTile];        // rh = fp32(1 / b)
+  __shared__ __align__(16) float lds_coll[kTile];        // rl = fp32((1 - b rh) rh)
+  float *lds_part = reinterpret_cast<float *>(lds_t);    // column partial maxima [rg][c] (8 KB)
+
+  const int t = threadIdx.x;
+  const int cc = t & 15, rg = t >> 4;
+  const int64_t bid = blockIdx.x;
+  const int64_t bj = bid / a.ni, bi = bid - bj * a.ni;
+  const int64_t r0 = bi * kTile + rg * 8;
+  const int64_t c0 = bj * kTile + cc * 8;
+  const bool valid = r0 < a.R && c0 < a.C;
+
+  u32x2 raw[8];
+  f32x4 s0 = (f32x4){0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  if (valid) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      raw[k] = *reinterpret_cast<const u32x2 *>(a.q + (r0 + k) * a.C + c0);
+    s0 = *reinterpret_cast<const f32x4 *>(a.s + bj * a.R + r0);
+    s1 = *reinterpret_cast<const f32x4 *>(a.s + bj * a.R + r0 + 4);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) raw[k] = (u32x2){0u, 0u};
+  }
+  const float sr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+
+  // dequantized elements: hardware e4m3 -> fp32 decode (exact), times the
+  // row scale
+  float d[8][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto p0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[k].x, false);
+    const auto p1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[k].x, true);
+    const auto p2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[k].y, false);
+    const auto p3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[k].y, true);
+    d[k][0] = p0[0] * sr[k]; d[k][1] = p0[1] * sr[k];
+    d[k][2] = p1[0] * sr[k]; d[k][3] = p1[1] * sr[k];
+    d[k][4] = p2[0] * sr[k]; d[k][5] = p2[1] * sr[k];
+    d[k][6] = p3[0] * sr[k]; d[k][7] = p3[1] * sr[k];
+  }
+
+  // column maxima of |d| over this thread's 8 rows (finite values: the
+  // absolute values are free source modifiers of the max instructions)
+  float cm[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = __builtin_fmaxf(m, __builtin_fabsf(d[k][c]));
+    cm[c] = m;
+  }
+  *reinterpret_cast<f32x4 *>(&lds_part[rg * kTile + cc * 8]) = (f32x4){cm[0], cm[1], cm[2], cm[3]};
+  *reinterpret_cast<f32x4 *>(&lds_part[rg * kTile + cc * 8 + 4]) = (f32x4){cm[4], cm[5], cm[6], cm[7]};
+  __syncthreads();
+
+  if (t < kTile) {
+    float m = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) m = fmaxf(m, lds_part[g * kTile + t]);
+    const float sc = tile_scale(m);
+    const float rh = 1.0f / sc;
+    lds_cols[t] = sc;
+    lds_colh[t] = rh;
+    lds_coll[t] = __builtin_fmaf(-rh, sc, 1.0f) * rh;
+    const int64_t cg = bj * kTile + t;
+    if (cg < a.C) a.st[bi * a.C + cg] = sc;
+  }
+  __syncthreads();
+
+  bool fast = true;
+  {
+    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&lds_cols[cc * 8]);
+    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&lds_cols[cc * 8 + 4]);
+    const float cs[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) fast &= cs[c] >= kRequantFastMin && cs[c] <= kRequantFastMax;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float b = lds_cols[cc * 8 + c], rh = lds_colh[cc * 8 + c], rl = lds_coll[cc * 8 + c];
+    float v[8];
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = quot_2w(d[k][c], b, rh, rl);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = d[k][c] / b;
+    }
+    u32x2 col;
+    col.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+    col.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
+    put_transposed_slot(lds_t, cc * 8 + c, rg, col);
+  }
+  __syncthreads();
+  flush_transposed<false>(lds_t, a.qt, a.R, a.C, bi, bj, t);
 }
 
 template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT>
@@ -305,6 +479,23 @@ hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, f
   a.s = s;
   if (q) return launch_quant<false, false, true, true, true>(a, stream);
   return launch_quant<false, false, true, false, true>(a, stream);
+}
+
+hipError_t run_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C, uint8_t *qt,
+                             float *st, hipStream_t stream) {
+  RequantArgs a{};
+  a.q = q;
+  a.s = s;
+  a.R = R;
+  a.C = C;
+  a.ni = (R + kTile - 1) / kTile;
+  a.nj = (C + kTile - 1) / kTile;
+  a.qt = qt;
+  a.st = st;
+  const int64_t blocks = a.ni * a.nj;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(requant_t_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace puro

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 1
+#define PURO_ABI_VERSION 2
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -120,6 +120,30 @@ puro_status puro_quant_w_128x128(const uint16_t *w, int64_t rows, int64_t cols,
 puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *qt, float *st, uint8_t *q_row, float *s_row,
                                  puro_stream_t stream);
+
+/*
+ * puro_requant_act_t -- transposed 128x1 codes rebuilt from saved 1x128 codes
+ * (for a backward pass that kept only the FP8 copy of an activation).  Where
+ * puro_quant_transpose quantizes the bf16 original along the other axis, this
+ * call dequantizes each saved code and quantizes the result again in 128x1
+ * tiles:
+ *   d[r][c]  = fp32(dec(q[r][c]) * s[c/128][r])      (exact product, one rounding)
+ *   st[i][c] = amax over rows 128i.. of |d[.][c]| / 448 (1 for an all-zero tile)
+ *   qt[c][r] = e4m3(fp32(d[r][c] / st[r/128][c]))    (IEEE division)
+ *   q    [rows][cols] uint8 codes (input), as puro_quant_act_1x128 writes them
+ *   s    [ceil(cols/128)][rows] fp32 scales (input), as puro_quant_act_1x128
+ *        writes them; every scale must be a positive normal fp32 value
+ *        (>= 2^-126), which the quantizer gives for every tile whose maximum is
+ *        0 or at least 2^-117; smaller scales and NaN codes are outside the
+ *        contract (not detected)
+ *   qt   [cols][rows] uint8 (output), st [ceil(rows/128)][cols] fp32 (output),
+ *        laid out as puro_quant_transpose(PURO_T_ACT) writes them
+ * Both rows and cols must be multiples of 16.  The result differs from
+ * quantizing the bf16 original (two roundings instead of one); it is what a
+ * pass that saved only q and s can compute.
+ */
+puro_status puro_requant_act_t(const uint8_t *q, const float *s, int64_t rows, int64_t cols,
+                               uint8_t *qt, float *st, puro_stream_t stream);
 
 /*
  * puro_gemm_workspace_bytes -- device workspace that puro_gemm_fp8_blockwise

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
-                            "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
+                            "puro_requant_act_t", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
                             "puro_status_str", "puro_abi_version"])
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 1
+    assert puro.puro_abi_version() == 2
     for s in range(10):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -90,6 +90,28 @@ def test_quant_transpose_validation():
     assert f(0, A0, 128, 128, A1, A2, A3 + 8, A4) == ALIGN
     assert f(0, A0, 128, 128, A1, A2, A1 + 1024, A4) == ALIAS  # q_row overlaps qt
     assert f(0, A0, 0, 128, None, None, None, None) == OK
+
+
+def test_requant_validation():
+    f = puro.puro_requant_act_t
+    assert f(A0, A1, 120, 128, A2, A3) == SHAPE               # rows must be a multiple of 16
+    assert f(A0, A1, 128, 100, A2, A3) == SHAPE
+    assert f(A0, A1, -16, 128, A2, A3) == SHAPE
+    assert f(A0, A1, 1 << 31, 128, A2, A3) == SHAPE
+    assert f(None, None, 0, 128, None, None) == OK            # empty: nothing to do
+    assert f(A0, A1, 128, 0, None, None) == OK
+    assert f(None, A1, 128, 128, A2, A3) == NULL
+    assert f(A0, None, 128, 128, A2, A3) == NULL
+    assert f(A0, A1, 128, 128, None, A3) == NULL
+    assert f(A0, A1, 128, 128, A2, None) == NULL
+    assert f(A0 + 8, A1, 128, 128, A2, A3) == ALIGN
+    assert f(A0, A1 + 4, 128, 128, A2, A3) == ALIGN
+    assert f(A0, A1, 128, 128, A2, A3 + 4) == ALIGN
+    assert f(A0, A1, 128, 128, A0 + 1024, A3) == ALIAS        # qt overlaps q
+    assert f(A0, A1, 128, 128, A2, A1 + 256) == ALIAS         # st overlaps s
+    assert f(A0, A1, 128, 128, A2, A2 + 4096) == ALIAS        # st inside qt
+    if no_gpu():
+        assert f(A0, A1, 128, 128, A2, A3) == DEVICE
 
 
 # ---------------------------------------------------------------- GEMM

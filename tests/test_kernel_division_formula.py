@@ -21,3 +21,17 @@ def test_reciprocal_division_gives_ieee_quotient_codes(tmp_path):
     pairs, bad = int(out[0]), int(out[1])
     assert pairs > 1_000_000_000
     assert bad == 0
+
+
+@pytest.mark.slow
+def test_requantizer_division_is_the_ieee_quotient(tmp_path):
+    """The requantizer divides arbitrary fp32 values (dequantized codes) by a
+    column scale with a two-word reciprocal and one residual correction; see
+    tests/csrc/requant_quotient_check.c for the argument and what is replayed."""
+    exe = str(tmp_path / "requant_quotient_check")
+    subprocess.run(["gcc", "-std=c99", "-O2", "-fopenmp", "-ffp-contract=off",
+                    os.path.join(HERE, "csrc", "requant_quotient_check.c"), "-o", exe, "-lm"], check=True)
+    out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    pairs, bad = int(out[0]), int(out[1])
+    assert pairs > 4_000_000_000
+    assert bad == 0
