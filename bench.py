@@ -15,9 +15,19 @@ Inputs are seeded synthetic tensors (see workloads.py) resident in HBM before
 the timed region.  The reported value is GEMM TFLOP/s over the whole step
 (quantizers included in the time).
 
+Other workloads (--workload):
+  layer_fp8_saved  the same layer step when the forward pass keeps only the
+                   1x128 FP8 codes of each input X: the wgrad operand X^T is
+                   rebuilt from them by the requantizer (dequantize, 128x1
+                   quantization of the transpose) instead of quantized from
+                   the bf16 X;
+  requant          the requantizer alone over the layer's four saved inputs
+                   (16384 x 2048 three times, 16384 x 6144): HBM GB/s;
+  qkv_fprop, mlp_fprop, mlp_down_bwd   single GEMM slices of the layer.
+
 Prints ONE JSON line.  Options: --steps K --warmup W (defaults 20 / 5),
 --gpus N (only 1 is supported: the path is measured on one GPU),
---workload {layer, qkv_fprop, mlp_fprop, mlp_down_bwd}, --no-cpu-baseline.
+--workload NAME, --no-cpu-baseline.
 """
 from __future__ import annotations
 
@@ -34,9 +44,14 @@ sys.path.insert(0, ROOT)
 PEAK_FP8_FLOPS = 5.0e15      # MI355X dense FP8 MFMA, published
 PEAK_HBM_BPS = 8.0e12        # MI355X HBM3E, published
 METRIC = "blockwise-FP8 GEMM TFLOP/s & % FP8 MFMA peak; quantizer GB/s, Puro-2B shapes"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "blockwise_fp8_gemm_act_amd", "csrc", f)
-                  for f in ("gemm.hip", "device_common.h")]
+_CSRC = os.path.join(ROOT, "blockwise_fp8_gemm_act_amd", "csrc")
+# rocprofv3 counter records per kernel family: the file and the sources its figures were taken on
+TRAFFIC = {
+    "gemm": (os.path.join(ROOT, "profiles", "gemm_traffic.json"),
+             [os.path.join(_CSRC, f) for f in ("gemm.hip", "device_common.h")]),
+    "requant": (os.path.join(ROOT, "profiles", "requant_traffic.json"),
+                [os.path.join(_CSRC, f) for f in ("quant.hip", "device_common.h")]),
+}
 
 
 def parse():
@@ -44,7 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="layer", choices=["layer", "qkv_fprop", "mlp_fprop", "mlp_down_bwd"])
+    ap.add_argument("--workload", default="layer",
+                    choices=["layer", "layer_fp8_saved", "requant", "qkv_fprop", "mlp_fprop", "mlp_down_bwd"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -109,6 +125,15 @@ def build_plan(workload, tensors, puro, torch):
                                bytes_=R * C * (2 + 1 + 4 / 16384)))
         return (q, s), None
 
+    def requant(saved, name):
+        q, s = saved
+        R, C = q.shape
+        qt, st = alloc((C, R), torch.uint8), alloc((cdiv(R, 128), C), torch.float32)
+        args = (q.data_ptr(), s.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(), stream)
+        launches.append(Launch("requant", name, lambda: check(puro.puro_requant_act_t(*args), name),
+                               bytes_=R * C * (2 + 4 / 128 + 4 / 128)))
+        return qt, st
+
     def gemm(mode, a, b, out_dtype, name):
         (aq, sa), (bq, sb) = a, b
         M, K = aq.shape
@@ -135,6 +160,26 @@ def build_plan(workload, tensors, puro, torch):
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
             gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad")
+    elif workload == "layer_fp8_saved":
+        from workloads import LINEARS
+        for lin in LINEARS:
+            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            xrow = q_act(x, lin + ".quant_x")
+            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            dyrow, dyt = q_act_dual(dy, lin + ".quant_dy")
+            gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
+            gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
+            xt = requant(xrow, lin + ".requant_x")
+            gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad")
+    elif workload == "requant":
+        # the saved codes are made once, outside the timed step
+        from workloads import LINEARS
+        for lin in LINEARS:
+            x = tensors["x_" + lin]
+            R, C = x.shape
+            q, s = alloc((R, C), torch.uint8), alloc((cdiv(C, 128), R), torch.float32)
+            check(puro.puro_quant_act_1x128(x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), stream), "setup")
+            requant((q, s), lin + ".requant_x")
     elif workload == "qkv_fprop":
         xrow = q_act(tensors["x"], "quant_x")
         wrow, _ = q_w_dual(tensors["w"], "quant_w", transposed=False)
@@ -156,15 +201,19 @@ def build_plan(workload, tensors, puro, torch):
 WORKLOAD_DESC = {
     "layer": ("Qwen3-1.7B-shaped layer (Puro-2B), 16384 tokens: QKV 2048->4096, O 2048->2048, "
               "gate_up 2048->12288, down 6144->2048; fprop+dgrad+wgrad and every quantize/transpose kernel"),
+    "layer_fp8_saved": ("the layer step (16384 tokens) with FP8-saved inputs: X quantized 1x128 only, the wgrad "
+                        "operand X^T requantized from those codes"),
+    "requant": ("requantization of the layer's saved 1x128 input codes into transposed 128x1 tiles, 16384 tokens: "
+                "X_qkv, X_o, X_gate_up [16384x2048], X_down [16384x6144]"),
     "qkv_fprop": "QKV projection fprop, 4096 tokens: X[4096x2048] x W[4096x2048]^T -> bf16",
     "mlp_fprop": "MLP fprop, 8192 tokens: gate_up X[8192x2048] x W[12288x2048]^T, down X[8192x6144] x W[2048x6144]^T",
     "mlp_down_bwd": "MLP down backward, 8192 tokens: dgrad dY[8192x2048] x W[2048x6144], wgrad dY^T x X[8192x6144]",
 }
 
 
-def source_hash():
+def source_hash(family="gemm"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in TRAFFIC[family][1]:
         with open(p, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -172,15 +221,52 @@ def source_hash():
 
 def load_traffic(kernel_kind):
     """HBM traffic per launch measured with rocprofv3 counters, if taken on the current kernel source."""
+    family = kernel_kind.split(":")[0]
+    if family not in TRAFFIC:
+        return None
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(TRAFFIC[family][0]) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash(family):
         return None
     ent = rec.get("kernels", {}).get(kernel_kind)
     return None if ent is None else ent.get("bytes_per_launch")
+
+
+def cpu_baseline_requant(tensors, budget_s):
+    """The oracle's requantizer (as it is) on the host cores over a bounded sample:
+    row slabs of the 16384 x 6144 input's saved codes, growing until about
+    `budget_s` seconds.  The saved codes of the sample come from the oracle's
+    own 1x128 quantizer (not timed)."""
+    import numpy as np
+    import oracle
+    from workloads import bits
+    oracle.build(force=False)
+    x = tensors["x_down"]
+    R, C = x.shape
+    qa, sa = oracle.quant_act_1x128(bits(x))          # 1x128 tiles: row slabs are independent
+    rows = 256
+    spent = 0.0
+    done = 0.0
+    while spent < budget_s:
+        q, s = qa[:rows], np.ascontiguousarray(sa[:, :rows])
+        t1 = time.perf_counter()
+        oracle.requant_act_t(q, s)
+        dt = time.perf_counter() - t1
+        spent += dt
+        done += rows * C * (2 + 4 / 128 + 4 / 128)
+        if dt < budget_s / 8 and rows < R:
+            rows = min(rows * 2, R)
+    return {
+        "value": round(done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "oracle requantization of row slabs (256 rows and up) of the 16384x6144 input's saved codes, "
+                  "%.0f MB of algorithmic traffic in %.1f s" % (done / 1e6, spent),
+    }
 
 
 def cpu_baseline(tensors, workload, budget_s):
@@ -244,13 +330,20 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
-    tensors = workloads.make(args.workload, seed=args.seed, device="cuda")
+    if args.workload in ("layer_fp8_saved", "requant"):
+        names = None if args.workload == "layer_fp8_saved" else {"x_" + lin for lin in workloads.LINEARS}
+        tensors = workloads.make("layer", seed=args.seed, device="cuda", names=names)
+    else:
+        tensors = workloads.make(args.workload, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
     launches, keep = build_plan(args.workload, tensors, puro, torch)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(tensors, args.workload, args.cpu_seconds)
+        if args.workload == "requant":
+            cpu = cpu_baseline_requant(tensors, args.cpu_seconds)
+        else:
+            cpu = cpu_baseline(tensors, args.workload, args.cpu_seconds)
 
     def step(events=None):
         for i, l in enumerate(launches):
@@ -264,23 +357,32 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(args.steps)]
+    # Events between launches cost a few microseconds each on the GPU timeline.
+    # A workload of a single kernel kind is timed without them (its roofline
+    # is then total algorithmic bytes over the step time), and its per-launch
+    # table comes from one extra untimed step with events.
+    single_kind = len({l.kind for l in launches}) == 1
+    n_ev = 1 if single_kind else args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(n_ev)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step(ev[s])
+        step(None if single_kind else ev[s])
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
+    if single_kind:
+        step(ev[0])
+        torch.cuda.synchronize()
 
     # per-launch durations (event before this launch -> event before the next)
     per = {}
-    for s in range(args.steps):
+    for s in range(n_ev):
         for i, l in enumerate(launches):
             d = ev[s][i].elapsed_time(ev[s][i + 1])
             per.setdefault(i, []).append(d)
@@ -307,10 +409,16 @@ def main():
     gemm_flops = sum(l.flops for l in launches)
     gemm_ms = sum(v["ms"] for k, v in kinds.items() if k.startswith("gemm"))
     quant = kinds.get("quant", {"ms": 0.0, "bytes": 0.0})
-    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    if gemm_flops:
+        value, unit, metric = gemm_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC
+    else:
+        step_bytes = sum(l.bytes for l in launches)
+        value, unit, metric = step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", "requantizer HBM GB/s, Puro-2B layer inputs"
 
     # dominant kernel: the launch type with the most time per step
     dom_kind, dom = max(((k, v) for k, v in kinds.items()), key=lambda kv: kv[1]["ms"])
+    if single_kind:
+        dom = dict(dom, ms=ms_per_step)
     if dom_kind.startswith("gemm"):
         achieved = dom["flops"] / (dom["ms"] * 1e-3)
         roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 1), "peak": PEAK_FP8_FLOPS / 1e12,
@@ -325,13 +433,15 @@ def main():
                                       else round(dom["bytes"] / dom["launches"] / 1e6, 3))
     roof["algorithmic_unit"] = "GFLOP" if dom_kind.startswith("gemm") else "MB"
     roof["avg_launch_ms"] = round(dom["ms"] / dom["launches"], 4)
+    roof["timing"] = ("HIP events around each timed step, no events between its launches" if single_kind
+                      else "HIP events between consecutive launches of each timed step")
     tr = load_traffic(dom_kind)
     roof["traffic"] = tr
 
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -339,15 +449,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 (fp32 accumulate)",
+        "dtype": "e4m3 (fp32 accumulate)" if gemm_flops else "e4m3 -> fp32 -> e4m3",
         "data": "synthetic (seeded, Puro-2B-shaped; see workloads.py)",
         "config": {"workload": WORKLOAD_DESC[args.workload], "name": args.workload,
-                   "tokens": {"layer": 16384, "qkv_fprop": 4096}.get(args.workload, 8192),
+                   "tokens": {"qkv_fprop": 4096, "mlp_fprop": 8192, "mlp_down_bwd": 8192}.get(args.workload, 16384),
                    "hidden": 2048, "parallelism": "single GPU"},
-        "pct_fp8_peak": round(100 * value * 1e12 / PEAK_FP8_FLOPS, 2),
+        "pct_fp8_peak": round(100 * value * 1e12 / PEAK_FP8_FLOPS, 2) if gemm_flops else None,
         "gemm_only_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1) if gemm_ms else None,
         "quant_gbps": round(quant["bytes"] / (quant["ms"] * 1e-3) / 1e9, 1) if quant["ms"] else None,
         "quant_pct_hbm_peak": round(100 * quant["bytes"] / (quant["ms"] * 1e-3) / PEAK_HBM_BPS, 1) if quant["ms"] else None,
+        "requant_gbps": (round(kinds["requant"]["bytes"] / (kinds["requant"]["ms"] * 1e-3) / 1e9, 1)
+                         if "requant" in kinds else None),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
         "cpu_baseline": cpu,

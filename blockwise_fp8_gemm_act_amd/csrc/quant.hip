@@ -45,7 +45,6 @@ __device__ __forceinline__ void put_transposed_slot(uint8_t *lds_t, int lc, int 
   *reinterpret_cast<u32x2 *>(&lds_t[lc * kTile + ((g ^ (lc >> 3)) * 8)]) = codes;
 }
 
-template <bool kNtStore>
 __device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *qt, int64_t R, int64_t C,
                                                  int64_t bi, int64_t bj, int t) {
 #pragma unroll
@@ -59,12 +58,8 @@ __device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *
     const int l = p ^ (xs >> 1);        // logical 16-byte chunk = rows 16l .. 16l+15
     const int64_t orow = bj * kTile + lc;
     const int64_t ocol = bi * kTile + l * 16;
-    if (orow < C && ocol < R) {
-      if constexpr (kNtStore)
-        __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(qt + orow * R + ocol));
-      else
-        *reinterpret_cast<u32x4 *>(qt + orow * R + ocol) = d;
-    }
+    if (orow < C && ocol < R)
+      __builtin_nontemporal_store(d, reinterpret_cast<u32x4 *>(qt + orow * R + ocol));
   }
 }
 
@@ -264,7 +259,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
       put_transposed_slot(lds_t, cc * 8 + c, rg, col);
     }
     __syncthreads();
-    flush_transposed<true>(lds_t, a.qt, a.R, a.C, bi, bj, t);
+    flush_transposed(lds_t, a.qt, a.R, a.C, bi, bj, t);
   }
 }
 
@@ -296,13 +291,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
 //
 // Memory order.  Consecutive workgroups walk down a block column (block row
 // index fastest), so the blocks in flight together write adjacent 128-byte
-// segments of the same output rows; loads and stores are ordinary cached
-// accesses.  Measured on MI355X for a 16384 x 6144 input, the same transposed
-// byte movement ran 31 us this way against 46 us with workgroups walking
-// along block rows and non-temporal accesses (a plain 100 MB device copy of
-// the same bytes: 28 us).  The partial column maxima share the LDS buffer of
-// the transposed codes (they are dead before the codes are staged), which
-// leaves room for more resident workgroups.
+// segments of the same output rows; loads and stores are non-temporal.
+// Measured on MI355X with inputs rotated over 1.2 GB (so that the 256 MB
+// last-level cache cannot serve them), a 16384 x 6144 input takes 42 us this
+// way against 48 us with workgroups walking along block rows; a plain device
+// copy of the same bytes takes 38 us.  The partial column maxima share the
+// LDS buffer of the transposed codes (they are dead before the codes are
+// staged), which leaves room for more resident workgroups.
 struct RequantArgs {
   const uint8_t *q;        // saved codes [R][C]
   const float *s;          // their 1x128 scales [nj][R]
@@ -344,7 +339,7 @@ __global__ __launch_bounds__(256) void requant_t_kernel(RequantArgs a) {
   if (valid) {
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      raw[k] = *reinterpret_cast<const u32x2 *>(a.q + (r0 + k) * a.C + c0);
+      raw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(a.q + (r0 + k) * a.C + c0));
     s0 = *reinterpret_cast<const f32x4 *>(a.s + bj * a.R + r0);
     s1 = *reinterpret_cast<const f32x4 *>(a.s + bj * a.R + r0 + 4);
   } else {
@@ -421,7 +416,7 @@ __global__ __launch_bounds__(256) void requant_t_kernel(RequantArgs a) {
     put_transposed_slot(lds_t, cc * 8 + c, rg, col);
   }
   __syncthreads();
-  flush_transposed<false>(lds_t, a.qt, a.R, a.C, bi, bj, t);
+  flush_transposed(lds_t, a.qt, a.R, a.C, bi, bj, t);
 }
 
 template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT>
