@@ -69,6 +69,9 @@ def _load():
                  "orc_quant_act_128x1_t", "orc_quant_w_128x128_t"):
         getattr(lib, name).argtypes = [P, I64, I64, P, P]
     lib.orc_requant_act_t.argtypes = [P, P, I64, I64, P, P]
+    lib.orc_swiglu_value.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    lib.orc_swiglu_value.restype = ctypes.c_uint16
+    lib.orc_swiglu.argtypes = [P, I64, I64, P]
     lib.orc_gemm_element.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, I64, I64]
     lib.orc_gemm_element.restype = ctypes.c_double
     lib.orc_gemm.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, I64, P]
@@ -203,6 +206,33 @@ def requant_act_t(q: np.ndarray, s: np.ndarray):
     st = np.empty((_cdiv(R, TILE), C), dtype=np.float32)
     _load().orc_requant_act_t(_ptr(q), _ptr(s), R, C, _ptr(qt), _ptr(st))
     return qt, st
+
+
+def swiglu_value(g: int, u: int) -> int:
+    """bf16 bits of bf16(silu(g) * u) for bf16 bit patterns g, u."""
+    return int(_load().orc_swiglu_value(int(g), int(u)))
+
+
+def swiglu(gu: np.ndarray) -> np.ndarray:
+    """gu: uint16 (bf16 bits) [R][2*I], gate then up -> h uint16 [R][I] = bf16(silu(gate) * up)."""
+    gu = _u16(gu)
+    R, C2 = gu.shape
+    if C2 % 2:
+        raise ValueError("the gate/up input needs an even number of columns")
+    h = np.empty((R, C2 // 2), dtype=np.uint16)
+    _load().orc_swiglu(_ptr(gu), R, C2 // 2, _ptr(h))
+    return h
+
+
+def swiglu_quant(gu: np.ndarray, dual: bool = False):
+    """SwiGLU then quantization of h: (q, s) as quant_act_1x128(h), plus (qt, st) as
+    quant_act_128x1_t(h) when dual.  Returns (h, q, s) or (h, q, s, qt, st)."""
+    h = swiglu(gu)
+    q, s = quant_act_1x128(h)
+    if not dual:
+        return h, q, s
+    qt, st = quant_act_128x1_t(h)
+    return h, q, s, qt, st
 
 
 # ---------------------------------------------------------------- GEMM

@@ -42,6 +42,8 @@
 
 #define TILE 128
 
+uint16_t orc_f64_to_bf16(double v);
+
 /* ------------------------------------------------------------------ */
 /* bf16 and e4m3 scalars                                               */
 /* ------------------------------------------------------------------ */
@@ -295,6 +297,43 @@ void orc_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C,
             for (r = r0; r < r1; ++r)
                 qt[c * R + r] = orc_quantize_value(deq_act_f32(q[r * C + c], s[j * R + r]), sc);
         }
+    }
+}
+
+/* SwiGLU of the gate/up projection output, rounded to bf16: the input of the
+ * MLP down projection.  The pages (roboind) keep activations in BF16 around
+ * the FP8 GEMMs; the model is Qwen3-shaped, whose MLP gates with SiLU.  With
+ * gate g and up u (both bf16),
+ *   h = bf16(silu(g) * u),  silu(g) = g / (1 + exp(-g)),
+ * evaluated in fp64 in that order (libm exp) and rounded once, to nearest
+ * even, to bf16.  That is the correctly rounded bf16 of the exact value
+ * except where the exact value lies within ~2^-50 (relative) of a bf16
+ * rounding midpoint; there the fp64 value decides.  Two systematic such
+ * classes: |g| < 2^-52, where fp64 gives silu(g) = g/2 exactly although the
+ * exact value is larger by about g^2/4, and g > 37, where fp64 gives
+ * silu(g) = g exactly although the exact value is smaller by about g e^-g;
+ * a g*u/2 (or g*u) on a midpoint then rounds to even instead of to the side
+ * the exact value lies on.
+ * gu: bf16 [R][2*I]; gate = gu[r][c], up = gu[r][I + c] for c < I (the
+ * first half of each row is the gate, the second the up projection).
+ * h: bf16 [R][I].  The 1x128 / 128x1 codes of h are those of
+ * orc_quant_act_1x128 / orc_quant_act_128x1_t applied to h. */
+uint16_t orc_swiglu_value(uint16_t g, uint16_t u)
+{
+    double gd = (double)orc_bf16_to_f32(g);
+    double ud = (double)orc_bf16_to_f32(u);
+    double silu = gd / (1.0 + exp(-gd));
+    return orc_f64_to_bf16(silu * ud);
+}
+
+void orc_swiglu(const uint16_t *gu, int64_t R, int64_t I, uint16_t *h)
+{
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < R; ++r) {
+        int64_t c;
+        for (c = 0; c < I; ++c)
+            h[r * I + c] = orc_swiglu_value(gu[r * 2 * I + c], gu[r * 2 * I + I + c]);
     }
 }
 
