@@ -46,6 +46,8 @@ _lib.puro_quant_w_128x128.restype = ctypes.c_int
 _lib.puro_quant_transpose.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.puro_quant_transpose.restype = ctypes.c_int
 _lib.puro_requant_act_t.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
+_lib.puro_swiglu_quant.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]
+_lib.puro_swiglu_quant.restype = ctypes.c_int
 _lib.puro_requant_act_t.restype = ctypes.c_int
 _lib.puro_gemm_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64, _I64]
 _lib.puro_gemm_workspace_bytes.restype = ctypes.c_size_t
@@ -80,6 +82,10 @@ def puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream=None)
 
 def puro_requant_act_t(q, s, rows, cols, qt, st, stream=None) -> int:
     return _lib.puro_requant_act_t(q, s, rows, cols, qt, st, stream)
+
+
+def puro_swiglu_quant(gu, rows, inter, q, s, qt, st, h, stream=None) -> int:
+    return _lib.puro_swiglu_quant(gu, rows, inter, q, s, qt, st, h, stream)
 
 
 def puro_gemm_workspace_bytes(mode, M, N, K) -> int:
@@ -184,6 +190,34 @@ def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=Non
     _check(puro_requant_act_t(q.data_ptr(), s.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
                               _stream(stream)), "puro_requant_act_t")
     return qt, st
+
+
+def swiglu_quant(gu: torch.Tensor, dual: bool = False, write_h: bool = False, stream=None):
+    """SwiGLU of a [R][2I] gate/up bf16 tensor (gate first) fused with quantization of
+    h = bf16(silu(gate) * up).  Returns (q, s) [+ (qt, st) when dual] [+ h when write_h]."""
+    _bf16_input(gu, "gu")
+    R, C2 = gu.shape
+    if C2 % 2:
+        raise ValueError("gu needs an even number of columns (gate then up)")
+    I = C2 // 2
+    dev = gu.device
+    q = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    s = torch.empty((_cdiv(I, TILE), R), dtype=torch.float32, device=dev)
+    qt = st = h = None
+    if dual:
+        qt = torch.empty((I, R), dtype=torch.uint8, device=dev)
+        st = torch.empty((_cdiv(R, TILE), I), dtype=torch.float32, device=dev)
+    if write_h:
+        h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+    _check(puro_swiglu_quant(gu.data_ptr(), R, I, q.data_ptr(), s.data_ptr(),
+                             qt.data_ptr() if dual else None, st.data_ptr() if dual else None,
+                             h.data_ptr() if write_h else None, _stream(stream)), "puro_swiglu_quant")
+    out = (q, s)
+    if dual:
+        out += (qt, st)
+    if write_h:
+        out += (h,)
+    return out
 
 
 def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):

@@ -160,6 +160,26 @@ puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t ro
   return launched(puro::run_quant_t_w(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
 }
 
+puro_status puro_swiglu_quant(const uint16_t *gu, int64_t rows, int64_t inter, uint8_t *q, float *s,
+                              uint8_t *qt, float *st, uint16_t *h, puro_stream_t stream) {
+  if (inter > kMaxDim / 2 || !shape_ok(rows, 2 * inter) || inter % 16 != 0) return PURO_ERR_SHAPE;
+  if ((qt == nullptr) != (st == nullptr)) return PURO_ERR_NULL;
+  const bool dual = qt != nullptr;
+  if (dual && rows % 16 != 0) return PURO_ERR_SHAPE;
+  if (rows == 0 || inter == 0) return PURO_OK;
+  if (!gu || !q || !s) return PURO_ERR_NULL;
+  if (!aligned16(gu) || !aligned16(q) || !aligned16(s)) return PURO_ERR_ALIGN;
+  if (dual && (!aligned16(qt) || !aligned16(st))) return PURO_ERR_ALIGN;
+  if (h && !aligned16(h)) return PURO_ERR_ALIGN;
+  const Range in[] = {rng(gu, rows * inter * 4)};
+  const Range out[] = {rng(q, rows * inter), rng(s, cdiv(inter, 128) * rows * 4),
+                       rng(qt, dual ? rows * inter : 0), rng(st, dual ? cdiv(rows, 128) * inter * 4 : 0),
+                       rng(h, h ? rows * inter * 2 : 0)};
+  if (any_alias(in, 1, out, 5)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_swiglu_quant(gu, rows, inter, q, s, qt, st, h, (hipStream_t)stream));
+}
+
 puro_status puro_requant_act_t(const uint8_t *q, const float *s, int64_t rows, int64_t cols,
                                uint8_t *qt, float *st, puro_stream_t stream) {
   if (!shape_ok(rows, cols) || cols % 16 != 0 || rows % 16 != 0) return PURO_ERR_SHAPE;

@@ -16,6 +16,8 @@ hipError_t run_quant_t_act(const uint16_t *x, int64_t R, int64_t C, uint8_t *qt,
                            uint8_t *q, float *s, hipStream_t stream);
 hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, float *st,
                          uint8_t *q, float *s, hipStream_t stream);
+hipError_t run_swiglu_quant(const uint16_t *gu, int64_t R, int64_t I, uint8_t *q, float *s, uint8_t *qt,
+                            float *st, uint16_t *h, hipStream_t stream);
 hipError_t run_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C, uint8_t *qt,
                              float *st, hipStream_t stream);
 

@@ -27,12 +27,52 @@ namespace puro {
 struct QuantArgs {
   const uint16_t *x;
   int64_t R, C;
+  int64_t ld;              // row stride of x in elements (C, or 2C for the gate/up input)
   int64_t ni, nj;          // ceil(R/128), ceil(C/128)
   uint8_t *q;              // row-major codes [R][C] (or null)
   float *s;                // scales of the row-major codes
   uint8_t *qt;             // transposed codes [C][R] (or null)
   float *st;               // scales of the transposed codes
+  uint16_t *h;             // SwiGLU output [R][C] in bf16 (or null)
 };
+
+// SwiGLU of one gate/up pair, h = bf16(silu(g) * u), silu(g) = g / (1 + e^-g).
+// The value is defined as the fp64 evaluation of that expression, rounded
+// once to bf16 (round to nearest even).
+//
+// Fast path, fp32: s = g * rcp(1 + expf(-g)) is within 2.94 * 2^-24 of
+// silu(g) (relative) for every bf16 g with |g| <= 64, measured exhaustively
+// on gfx950 against fp64; with the rounding of p = s * u, p is within 3.44
+// fp32 ulps of the exact product.  So unless p's low 16 bits lie within 5
+// ulps of the bf16 rounding midpoint (0x8000), rounding p gives the bf16 of
+// the exact value, which the fp64 value rounds to as well.  Otherwise, or for
+// |g| > 64, the element takes the fp64 evaluation (swiglu_f64).
+__device__ __forceinline__ uint32_t swiglu_fast(float g, float u, bool &slow) {
+  const float e = expf(-g);
+  const float sg = g * __builtin_amdgcn_rcpf(1.0f + e);
+  const float p = sg * u;
+  const uint32_t b = __float_as_uint(p);
+  slow = ((b & 0xffffu) - 0x7ffbu) <= 10u || !(__builtin_fabsf(g) <= 64.0f);
+  return (b + 0x8000u) >> 16;
+}
+
+// bf16 bits of v, round to nearest even (from fp64: one rounding).
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
+  const uint32_t sign = signbit(v) ? 0x8000u : 0u;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (a < 0x1p-126) return sign | (uint32_t)rint(ldexp(a, 133));   // 2^-133 grid
+  int e = ilogb(a);
+  double n = rint(ldexp(a, 7 - e));                                 // 128 .. 256
+  if (n == 256.0) { n = 128.0; ++e; }
+  if (e > 127) return sign | 0x7f80u;
+  return sign | ((uint32_t)(e + 127) << 7) | ((uint32_t)n - 128u);
+}
+
+__device__ __forceinline__ uint32_t swiglu_f64(float g, float u) {
+  const double gd = g, ud = u;
+  return f64_to_bf16_bits(gd / (1.0 + exp(-gd)) * ud);
+}
 
 // Transposed codes of one 128x128 block, staged in LDS, to global memory.
 // LDS row c (a column of the block, an output row) holds 16 slots of 8 codes
@@ -63,10 +103,12 @@ __device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *
   }
 }
 
-// kRow:   1x128 scales (per row of the block)       -> row-major output
-// kCol:   128x1 scales (per column of the block)    -> transposed output
-// kBlock: one 128x128 scale                         -> row-major and/or transposed output
-template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT>
+// kRow:    1x128 scales (per row of the block)       -> row-major output
+// kCol:    128x1 scales (per column of the block)    -> transposed output
+// kBlock:  one 128x128 scale                         -> row-major and/or transposed output
+// kSwiGLU: the block's values are h = SwiGLU(gate, up) of a [R][2C] gate/up
+//          input (gate = first C columns), computed in registers
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
   __shared__ float lds_part[16 * kTile];                 // column partial maxima [rg][c]
   __shared__ float lds_rowamax[kTile];
@@ -85,13 +127,66 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
 
   // ---- load 8 rows x 8 columns (16 B per row), all in flight at once
   u32x4 raw[8];
+  if constexpr (kSwiGLU) {
+    // gate and up words of the same 8 x 8 block, then h in registers
+    u32x4 gw[8], uw[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int64_t r = r0 + k;
-    if (cvalid && r < a.R)
-      raw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + r * a.C + c0));
-    else
-      raw[k] = (u32x4){0u, 0u, 0u, 0u};
+    for (int k = 0; k < 8; ++k) {
+      const int64_t r = r0 + k;
+      if (cvalid && r < a.R) {
+        gw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + r * a.ld + c0));
+        uw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + r * a.ld + a.C + c0));
+      } else {
+        gw[k] = (u32x4){0u, 0u, 0u, 0u};
+        uw[k] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+    uint64_t slow = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bool s0, s1;
+        const uint32_t h0 = swiglu_fast(bf16lo(gw[k][j]), bf16lo(uw[k][j]), s0);
+        const uint32_t h1 = swiglu_fast(bf16hi(gw[k][j]), bf16hi(uw[k][j]), s1);
+        raw[k][j] = (h0 & 0xffffu) | (h1 << 16);
+        slow |= ((uint64_t)s0 << (k * 8 + 2 * j)) | ((uint64_t)s1 << (k * 8 + 2 * j + 1));
+      }
+    }
+    // rare elements near a bf16 rounding midpoint, or with |g| > 64: fp64,
+    // one element at a time (reloaded; the lines are still cached)
+    while (slow) {
+      const int i = __builtin_ctzll(slow);
+      slow &= slow - 1;
+      const int k = i >> 3, c = i & 7;
+      const int64_t off = (r0 + k) * a.ld + c0 + c;
+      const uint32_t hb = swiglu_f64(bf16lo(a.x[off]), bf16lo(a.x[off + a.C]));
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = raw[kk][j];
+          const uint32_t merged = (c & 1) ? ((w & 0xffffu) | (hb << 16)) : ((w & 0xffff0000u) | hb);
+          raw[kk][j] = (kk == k && j == (c >> 1)) ? merged : w;
+        }
+    }
+    if (a.h != nullptr) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t r = r0 + k;
+        if (cvalid && r < a.R)
+          __builtin_nontemporal_store(raw[k], reinterpret_cast<u32x4 *>(a.h + r * a.C + c0));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t r = r0 + k;
+      if (cvalid && r < a.R)
+        raw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(a.x + r * a.ld + c0));
+      else
+        raw[k] = (u32x4){0u, 0u, 0u, 0u};
+    }
   }
   // Hide the packed words from the optimizer between phases so that unpacked
   // values are recomputed in each phase instead of staying live across it.
@@ -419,11 +514,11 @@ __global__ __launch_bounds__(256) void requant_t_kernel(RequantArgs a) {
   flush_transposed(lds_t, a.qt, a.R, a.C, bi, bj, t);
 }
 
-template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT>
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false>
 static hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   const int64_t blocks = a.ni * a.nj;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((quant_block_kernel<kRow, kCol, kBlock, kWriteRow, kWriteT>),
+  hipLaunchKernelGGL((quant_block_kernel<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU>),
                      dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -433,6 +528,7 @@ static QuantArgs make_args(const uint16_t *x, int64_t R, int64_t C) {
   a.x = x;
   a.R = R;
   a.C = C;
+  a.ld = C;
   a.ni = (R + kTile - 1) / kTile;
   a.nj = (C + kTile - 1) / kTile;
   return a;
@@ -474,6 +570,19 @@ hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, f
   a.s = s;
   if (q) return launch_quant<false, false, true, true, true>(a, stream);
   return launch_quant<false, false, true, false, true>(a, stream);
+}
+
+hipError_t run_swiglu_quant(const uint16_t *gu, int64_t R, int64_t I, uint8_t *q, float *s, uint8_t *qt,
+                            float *st, uint16_t *h, hipStream_t stream) {
+  QuantArgs a = make_args(gu, R, I);
+  a.ld = 2 * I;
+  a.q = q;
+  a.s = s;
+  a.qt = qt;
+  a.st = st;
+  a.h = h;
+  if (qt) return launch_quant<true, true, false, true, true, true>(a, stream);
+  return launch_quant<true, false, false, true, false, true>(a, stream);
 }
 
 hipError_t run_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C, uint8_t *qt,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 2
+#define PURO_ABI_VERSION 3
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -144,6 +144,32 @@ puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t ro
  */
 puro_status puro_requant_act_t(const uint8_t *q, const float *s, int64_t rows, int64_t cols,
                                uint8_t *qt, float *st, puro_stream_t stream);
+
+/*
+ * puro_swiglu_quant -- SwiGLU of the MLP's gate/up projection output fused
+ * with the quantization of the result, the down projection's input.  The
+ * pages train a Qwen3-shaped model with BF16 activations around FP8 GEMMs
+ * (en.roboind.com article on Puro-2B, section "FP8 takes advantage of the RTX
+ * 5090's low precision efficiency"); its MLP gates with SiLU.  Per element,
+ *   h[r][c] = bf16(silu(g) * u),  g = gu[r][c], u = gu[r][inter + c],
+ *   silu(g) = g / (1 + e^-g), the value being that of the expression
+ *   evaluated in fp64, rounded once to bf16 (to nearest even),
+ * and h is quantized exactly as puro_quant_act_1x128 (and, optionally, the
+ * transposed 128x1 form of puro_quant_transpose(PURO_T_ACT)) would quantize
+ * it, without h passing through memory.
+ *   gu   [rows][2*inter] bf16 (input): gate in the first inter columns of a
+ *        row, up in the last inter (the halves of a fused gate/up weight)
+ *   q, s [rows][inter] codes, [ceil(inter/128)][rows] scales (outputs)
+ *   qt, st (optional, both NULL or both set): [inter][rows] codes and
+ *        [ceil(rows/128)][inter] scales of the 128x1 tiles of h (the down
+ *        projection's wgrad operand)
+ *   h    (optional, NULL to skip): [rows][inter] bf16, the SwiGLU values
+ * inter must be a multiple of 16, and rows too when qt is requested.  Inputs
+ * must be finite with every |silu(g) u| below 2^127.
+ */
+puro_status puro_swiglu_quant(const uint16_t *gu, int64_t rows, int64_t inter,
+                              uint8_t *q, float *s, uint8_t *qt, float *st, uint16_t *h,
+                              puro_stream_t stream);
 
 /*
  * puro_gemm_workspace_bytes -- device workspace that puro_gemm_fp8_blockwise

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
-                            "puro_requant_act_t", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
+                            "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
                             "puro_status_str", "puro_abi_version"])
 
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 2
+    assert puro.puro_abi_version() == 3
     for s in range(10):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -112,6 +112,28 @@ def test_requant_validation():
     assert f(A0, A1, 128, 128, A2, A2 + 4096) == ALIAS        # st inside qt
     if no_gpu():
         assert f(A0, A1, 128, 128, A2, A3) == DEVICE
+
+
+def test_swiglu_quant_validation():
+    f = puro.puro_swiglu_quant
+    assert f(A0, 128, 100, A1, A2, None, None, None) == SHAPE             # inter not a multiple of 16
+    assert f(A0, 120, 128, A1, A2, A3, A4, None) == SHAPE                 # rows must be a multiple of 16 for qt
+    assert f(A0, -1, 128, A1, A2, None, None, None) == SHAPE
+    assert f(A0, 16, 1 << 30, A1, A2, None, None, None) == SHAPE          # 2 * inter over the dimension limit
+    assert f(A0, 120, 128, A1, A2, None, None, None) != SHAPE             # rows free without qt
+    assert f(None, 0, 128, None, None, None, None, None) == OK
+    assert f(A0, 128, 128, A1, A2, A3, None, None) == NULL                # qt without st
+    assert f(None, 128, 128, A1, A2, None, None, None) == NULL
+    assert f(A0, 128, 128, None, A2, None, None, None) == NULL
+    assert f(A0, 128, 128, A1, None, None, None, None) == NULL
+    assert f(A0 + 8, 128, 128, A1, A2, None, None, None) == ALIGN
+    assert f(A0, 128, 128, A1, A2, None, None, A5 + 2) == ALIGN           # h misaligned
+    assert f(A0, 128, 128, A1, A2, A3 + 4, A4, None) == ALIGN
+    assert f(A0, 128, 128, A0 + 4096, A2, None, None, None) == ALIAS      # q inside gu
+    assert f(A0, 128, 128, A1, A2, None, None, A1 + 64) == ALIAS          # h overlaps q
+    assert f(A0, 128, 128, A1, A2, A3, A3 + 1024, None) == ALIAS          # st inside qt
+    if no_gpu():
+        assert f(A0, 128, 128, A1, A2, A3, A4, A5) == DEVICE
 
 
 # ---------------------------------------------------------------- GEMM

@@ -104,7 +104,7 @@ def _w(name, rows, cols):
     return Spec(name, (rows, cols), "weight")
 
 
-# The five workloads.  Each maps to the tensors it needs.
+# The workloads.  Each maps to the tensors it needs.
 WORKLOADS = {
     # 256x256 activations (2 outlier channels) against a 512x256 weight, fp32 out.
     "tiny_fprop": [_act("x", 256, 256, outliers=2), _w("w", 512, 256)],
@@ -116,6 +116,9 @@ WORKLOADS = {
     # MLP down-projection backward at 8192 tokens: dgrad and wgrad.
     "mlp_down_bwd": [Spec("dy", (8192, HIDDEN), "grad"), _w("w", HIDDEN, INTER),
                      Spec("x", (8192, INTER), "silu")],
+    # The MLP's gate/up projection output at 16384 tokens (gate then up, 2 x 6144
+    # columns): the input of the SwiGLU that feeds the down projection.
+    "mlp_swiglu": [Spec("gu", (16384, 2 * INTER), "act", outliers=0)],
     # One whole layer's four linears at 16384 tokens, forward and backward.
     "layer": [t for lin, (kin, kout) in LINEARS.items() for t in (
         _act(f"x_{lin}", 16384, kin), _w(f"w_{lin}", kout, kin),
