@@ -23,9 +23,13 @@ Other workloads (--workload):
                    the bf16 X;
   requant          the requantizer alone over the layer's four saved inputs
                    (16384 x 2048 three times, 16384 x 6144): HBM GB/s;
+  swiglu_quant     the fused SwiGLU + 1x128 / 128x1 quantization of the MLP's
+                   gate/up output at 16384 tokens (16384 x 12288 in, the down
+                   projection's two operands out): HBM GB/s;
   qkv_fprop, mlp_fprop, mlp_down_bwd   single GEMM slices of the layer.
 
-Prints ONE JSON line.  Options: --steps K --warmup W (defaults 20 / 5),
+Prints ONE JSON line.  Options: --steps K --warmup W (defaults 30 / 10 for the
+layer workloads, 300 / 300 for the single-kernel ones),
 --gpus N (only 1 is supported: the path is measured on one GPU),
 --workload NAME, --no-cpu-baseline.
 """
@@ -51,20 +55,32 @@ TRAFFIC = {
              [os.path.join(_CSRC, f) for f in ("gemm.hip", "device_common.h")]),
     "requant": (os.path.join(ROOT, "profiles", "requant_traffic.json"),
                 [os.path.join(_CSRC, f) for f in ("quant.hip", "device_common.h")]),
+    "swiglu_quant": (os.path.join(ROOT, "profiles", "swiglu_quant_traffic.json"),
+                     [os.path.join(_CSRC, f) for f in ("quant.hip", "device_common.h")]),
 }
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 30, or 300 for a single-kernel workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: 10, or 300 for a single-kernel workload)")
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "layer_fp8_saved", "requant", "qkv_fprop", "mlp_fprop", "mlp_down_bwd"])
+                    choices=["layer", "layer_fp8_saved", "requant", "swiglu_quant", "qkv_fprop", "mlp_fprop",
+                             "mlp_down_bwd"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # A single-kernel step lasts ~0.1 ms: a few hundred untimed steps first let the
+    # clocks settle (5 of them left the fused SwiGLU kernel ~10% slower), and the
+    # timed region still lasts only tens of milliseconds.
+    micro = args.workload in ("requant", "swiglu_quant")
+    if args.warmup is None:
+        args.warmup = 300 if micro else 10
+    if args.steps is None:
+        args.steps = 300 if micro else 30
+    return args
 
 
 def cdiv(a, b):
@@ -134,6 +150,16 @@ def build_plan(workload, tensors, puro, torch):
                                bytes_=R * C * (2 + 4 / 128 + 4 / 128)))
         return qt, st
 
+    def swiglu(gu, name):
+        R, C2 = gu.shape
+        I = C2 // 2
+        q, s = alloc((R, I), torch.uint8), alloc((cdiv(I, 128), R), torch.float32)
+        qt, st = alloc((I, R), torch.uint8), alloc((cdiv(R, 128), I), torch.float32)
+        args = (gu.data_ptr(), R, I, q.data_ptr(), s.data_ptr(), qt.data_ptr(), st.data_ptr(), None, stream)
+        launches.append(Launch("swiglu_quant", name, lambda: check(puro.puro_swiglu_quant(*args), name),
+                               bytes_=R * I * (4 + 2 * (1 + 4 / 128))))
+        return (q, s), (qt, st)
+
     def gemm(mode, a, b, out_dtype, name):
         (aq, sa), (bq, sb) = a, b
         M, K = aq.shape
@@ -180,6 +206,8 @@ def build_plan(workload, tensors, puro, torch):
             q, s = alloc((R, C), torch.uint8), alloc((cdiv(C, 128), R), torch.float32)
             check(puro.puro_quant_act_1x128(x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), stream), "setup")
             requant((q, s), lin + ".requant_x")
+    elif workload == "swiglu_quant":
+        swiglu(tensors["gu"], "down.swiglu_quant")
     elif workload == "qkv_fprop":
         xrow = q_act(tensors["x"], "quant_x")
         wrow, _ = q_w_dual(tensors["w"], "quant_w", transposed=False)
@@ -205,6 +233,8 @@ WORKLOAD_DESC = {
                         "operand X^T requantized from those codes"),
     "requant": ("requantization of the layer's saved 1x128 input codes into transposed 128x1 tiles, 16384 tokens: "
                 "X_qkv, X_o, X_gate_up [16384x2048], X_down [16384x6144]"),
+    "swiglu_quant": ("fused SwiGLU of the MLP gate/up output [16384x12288] (gate first) with 1x128 and 128x1 "
+                     "quantization of h [16384x6144], the down projection's fprop and wgrad operands"),
     "qkv_fprop": "QKV projection fprop, 4096 tokens: X[4096x2048] x W[4096x2048]^T -> bf16",
     "mlp_fprop": "MLP fprop, 8192 tokens: gate_up X[8192x2048] x W[12288x2048]^T, down X[8192x6144] x W[2048x6144]^T",
     "mlp_down_bwd": "MLP down backward, 8192 tokens: dgrad dY[8192x2048] x W[2048x6144], wgrad dY^T x X[8192x6144]",
@@ -269,6 +299,36 @@ def cpu_baseline_requant(tensors, budget_s):
     }
 
 
+def cpu_baseline_swiglu(tensors, budget_s):
+    """The oracle's SwiGLU and quantizers (as they are) on the host cores over
+    row slabs of the gate/up input, growing until about `budget_s` seconds."""
+    import oracle
+    from workloads import bits
+    oracle.build(force=False)
+    gu = bits(tensors["gu"])
+    R, C2 = gu.shape
+    I = C2 // 2
+    rows = 128
+    spent = 0.0
+    done = 0.0
+    while spent < budget_s:
+        t1 = time.perf_counter()
+        oracle.swiglu_quant(gu[:rows], dual=True)
+        dt = time.perf_counter() - t1
+        spent += dt
+        done += rows * I * (4 + 2 * (1 + 4 / 128))
+        if dt < budget_s / 8 and rows < R:
+            rows = min(rows * 2, R)
+    return {
+        "value": round(done / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": "oracle SwiGLU + 1x128 + 128x1 quantization of row slabs (128 rows and up) of the 16384x12288 "
+                  "gate/up input, %.0f MB of algorithmic traffic in %.1f s" % (done / 1e6, spent),
+    }
+
+
 def cpu_baseline(tensors, workload, budget_s):
     """The oracle (as it is) on a bounded sample of the same work, on the host cores:
     quantize the gate_up (or first) linear's X and W in full, then compute a
@@ -330,7 +390,9 @@ def main():
     import workloads
 
     torch.cuda.set_device(0)
-    if args.workload in ("layer_fp8_saved", "requant"):
+    if args.workload == "swiglu_quant":
+        tensors = workloads.make("mlp_swiglu", seed=args.seed, device="cuda")
+    elif args.workload in ("layer_fp8_saved", "requant"):
         names = None if args.workload == "layer_fp8_saved" else {"x_" + lin for lin in workloads.LINEARS}
         tensors = workloads.make("layer", seed=args.seed, device="cuda", names=names)
     else:
@@ -342,6 +404,8 @@ def main():
     if not args.no_cpu_baseline:
         if args.workload == "requant":
             cpu = cpu_baseline_requant(tensors, args.cpu_seconds)
+        elif args.workload == "swiglu_quant":
+            cpu = cpu_baseline_swiglu(tensors, args.cpu_seconds)
         else:
             cpu = cpu_baseline(tensors, args.workload, args.cpu_seconds)
 
@@ -413,7 +477,9 @@ def main():
         value, unit, metric = gemm_flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s", METRIC
     else:
         step_bytes = sum(l.bytes for l in launches)
-        value, unit, metric = step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s", "requantizer HBM GB/s, Puro-2B layer inputs"
+        value, unit = step_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        metric = {"requant": "requantizer HBM GB/s, Puro-2B layer inputs",
+                  "swiglu_quant": "fused SwiGLU + quantizer HBM GB/s, Puro-2B MLP"}[args.workload]
 
     # dominant kernel: the launch type with the most time per step
     dom_kind, dom = max(((k, v) for k, v in kinds.items()), key=lambda kv: kv[1]["ms"])
@@ -449,7 +515,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 (fp32 accumulate)" if gemm_flops else "e4m3 -> fp32 -> e4m3",
+        "dtype": ("e4m3 (fp32 accumulate)" if gemm_flops else
+                  {"requant": "e4m3 -> fp32 -> e4m3", "swiglu_quant": "bf16 -> fp32 (fp64 near ties) -> e4m3"}[args.workload]),
         "data": "synthetic (seeded, Puro-2B-shaped; see workloads.py)",
         "config": {"workload": WORKLOAD_DESC[args.workload], "name": args.workload,
                    "tokens": {"qkv_fprop": 4096, "mlp_fprop": 8192, "mlp_down_bwd": 8192}.get(args.workload, 16384),
