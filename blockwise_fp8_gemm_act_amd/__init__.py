@@ -8,7 +8,8 @@ importing this package fails.
 
 The raw C calls keep their C names (``puro_quant_act_1x128``,
 ``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_requant_act_t``,
-``puro_gemm_fp8_blockwise``, ...) and take integer device pointers.  The
+``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_accumulate``, ...) and take
+integer device pointers.  The
 tensor-level helpers ``quant_act_1x128``, ``quant_w_128x128``,
 ``quant_transpose``, ``requant_act_t``, ``gemm_fp8_blockwise`` allocate
 outputs with torch and call them on the current stream.
@@ -54,6 +55,9 @@ _lib.puro_gemm_workspace_bytes.restype = ctypes.c_size_t
 _lib.puro_gemm_fp8_blockwise.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
                                          _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
 _lib.puro_gemm_fp8_blockwise.restype = ctypes.c_int
+_lib.puro_gemm_fp8_blockwise_accumulate.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P,
+                                                    _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
+_lib.puro_gemm_fp8_blockwise_accumulate.restype = ctypes.c_int
 _lib.puro_status_str.argtypes = [ctypes.c_int]
 _lib.puro_status_str.restype = ctypes.c_char_p
 _lib.puro_abi_version.argtypes = []
@@ -96,6 +100,12 @@ def puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspa
                             stream=None) -> int:
     return _lib.puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspace,
                                         workspace_bytes, stream)
+
+
+def puro_gemm_fp8_blockwise_accumulate(mode, a, sa, b, sb, out, M, N, K, workspace, workspace_bytes,
+                                       stream=None) -> int:
+    return _lib.puro_gemm_fp8_blockwise_accumulate(mode, a, sa, b, sb, out, M, N, K, workspace,
+                                                   workspace_bytes, stream)
 
 
 def puro_status_str(status: int) -> str:
@@ -245,4 +255,23 @@ def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=No
     _check(puro_gemm_fp8_blockwise(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
                                    out.data_ptr(), od, M, N, K, wptr, wbytes, _stream(stream)),
            "puro_gemm_fp8_blockwise")
+    return out
+
+
+def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, workspace=None, stream=None):
+    """out (fp32 [M][N]) += the blockwise-scaled FP8 GEMM of a [M][K] and b [N][K]; returns out."""
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of shape [M][N]")
+    need = puro_gemm_workspace_bytes(mode, M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+    wptr = workspace.data_ptr() if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(puro_gemm_fp8_blockwise_accumulate(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                                              out.data_ptr(), M, N, K, wptr, wbytes, _stream(stream)),
+           "puro_gemm_fp8_blockwise_accumulate")
     return out

@@ -199,10 +199,13 @@ size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int6
   return puro::plan_gemm((int)mode, M, N, K).ws_bytes;
 }
 
-puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const float *sa,
-                                    const uint8_t *b, const float *sb, void *out,
-                                    puro_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
-                                    void *workspace, size_t workspace_bytes, puro_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                      void *out, puro_out_dtype out_dtype, bool accumulate, int64_t M, int64_t N, int64_t K,
+                      void *workspace, size_t workspace_bytes, puro_stream_t stream) {
   if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_F32 && out_dtype != PURO_OUT_BF16) return PURO_ERR_DTYPE;
   if (!shape_ok(M, K) || !shape_ok(N, K) || !shape_ok(M, N) || K % 16 != 0 || K > kMaxGemmK)
@@ -229,8 +232,26 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const
     if (plan.ws_bytes > 0 && workspace_bytes < plan.ws_bytes) return PURO_ERR_WORKSPACE;
   }
   if (puro_status d = check_device()) return d;
-  return launched(puro::run_gemm((int)mode, a, sa, b, sb, out, out_dtype == PURO_OUT_BF16, M, N, K,
+  return launched(puro::run_gemm((int)mode, a, sa, b, sb, out, out_dtype == PURO_OUT_BF16, accumulate, M, N, K,
                                  workspace, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const float *sa,
+                                    const uint8_t *b, const float *sb, void *out,
+                                    puro_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                    void *workspace, size_t workspace_bytes, puro_stream_t stream) {
+  return gemm_call(mode, a, sa, b, sb, out, out_dtype, false, M, N, K, workspace, workspace_bytes, stream);
+}
+
+puro_status puro_gemm_fp8_blockwise_accumulate(puro_gemm_mode mode, const uint8_t *a, const float *sa,
+                                               const uint8_t *b, const float *sb, float *out,
+                                               int64_t M, int64_t N, int64_t K,
+                                               void *workspace, size_t workspace_bytes, puro_stream_t stream) {
+  return gemm_call(mode, a, sa, b, sb, out, PURO_OUT_F32, true, M, N, K, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -37,7 +37,12 @@
 //    alone (a rotation by (item % 8) / 8 of its K range, which keeps the
 //    items that share an XCD's L2 in lockstep and staggers the 8 XCDs);
 //    optional split-K writes fp32 partials to a workspace that a second
-//    kernel sums in a fixed order.  Results are deterministic.
+//    kernel sums in a fixed order.  Results are deterministic;
+//  - accumulate mode (fp32 out): out = fp32(out + GEMM), one addition of the
+//    finished GEMM value per element, in the store epilogue or, with split-K,
+//    in the reduction.  It lets micro-batches add their weight gradients into
+//    one fp32 buffer (the pages tune micro-batch sizes per pipeline stage:
+//    en.roboind.com article, section "Unit cost, higher computing power").
 #include "device_common.h"
 #include "launch.h"
 
@@ -201,8 +206,9 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 // slices as one stream: the first slice of the next item is copied while the
 // last slice of the current one is computed, and the current item's output
 // leaves with direct global stores that drain while the next item computes.
-template <bool kRowScaledB, bool kBf16Out, bool kToWs>
+template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
+  static_assert(!kAcc || (!kBf16Out && !kToWs), "accumulate mode stores fp32 directly");
   // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
   __shared__ __align__(1024) uint8_t smem[2][2][kSliceBytes];
   __shared__ __align__(16) float sscale[2][2][kBM];
@@ -496,8 +502,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           float *ob = o + (int64_t)(mb * 16) * g.N;
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
-            *reinterpret_cast<v4f *>(ob + loff + 32 * pp) = acc[mb][2 * pp];
-            *reinterpret_cast<v4f *>(ob + loff + 32 * pp + 4) = acc[mb][2 * pp + 1];
+            v4f *p0 = reinterpret_cast<v4f *>(ob + loff + 32 * pp);
+            v4f *p1 = reinterpret_cast<v4f *>(ob + loff + 32 * pp + 4);
+            if constexpr (kAcc) {
+              const v4f o0 = *p0, o1 = *p1;
+              *p0 = o0 + acc[mb][2 * pp];
+              *p1 = o1 + acc[mb][2 * pp + 1];
+            } else {
+              *p0 = acc[mb][2 * pp];
+              *p1 = acc[mb][2 * pp + 1];
+            }
           }
         }
       } else {
@@ -512,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
             float *d = ob + (int64_t)fr * g.N + colB(nb);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < g.N) d[e] = acc[mb][nb][e];
+              if (n + e < g.N) d[e] = kAcc ? d[e] + acc[mb][nb][e] : acc[mb][nb][e];
           }
         }
       }
@@ -561,15 +575,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   }
 }
 
-// Sum of the split-K partials in increasing split order.
-template <bool kBf16Out>
+// Sum of the split-K partials in increasing split order (then added to the
+// fp32 output in accumulate mode).
+template <bool kBf16Out, bool kAcc = false>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, void *out, int64_t MN, int splits) {
+  static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
     float v = ws[i];
     for (int s = 1; s < splits; ++s) v += ws[(int64_t)s * MN + i];
     if constexpr (kBf16Out)
       reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else if constexpr (kAcc)
+      reinterpret_cast<float *>(out)[i] += v;
     else
       reinterpret_cast<float *>(out)[i] = v;
   }
@@ -638,11 +656,12 @@ static int compute_units() {
 }
 
 hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
-                    void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, void *ws,
+                    void *out, bool bf16_out, bool accumulate, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const int64_t MN = M * N;
   if (K == 0) {
+    if (accumulate) return hipSuccess;            // out + 0
     const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 65536);
     if (bf16_out) hipLaunchKernelGGL(fill_zero_kernel<true>, dim3(blocks), dim3(256), 0, stream, out, MN);
     else hipLaunchKernelGGL(fill_zero_kernel<false>, dim3(blocks), dim3(256), 0, stream, out, MN);
@@ -659,19 +678,27 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   const bool to_ws = p.splits > 1;
 #define PURO_LAUNCH(RB, BF, WS) \
   hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, BF, WS>), grid, dim3(kThreads), 0, stream, g)
+#define PURO_LAUNCH_ACC(RB) \
+  hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, true>), grid, dim3(kThreads), 0, stream, g)
   if (to_ws) {
     if (row_b) PURO_LAUNCH(true, false, true); else PURO_LAUNCH(false, false, true);
+  } else if (accumulate) {
+    if (row_b) PURO_LAUNCH_ACC(true); else PURO_LAUNCH_ACC(false);
   } else if (bf16_out) {
     if (row_b) PURO_LAUNCH(true, true, false); else PURO_LAUNCH(false, true, false);
   } else {
     if (row_b) PURO_LAUNCH(true, false, false); else PURO_LAUNCH(false, false, false);
   }
 #undef PURO_LAUNCH
+#undef PURO_LAUNCH_ACC
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !to_ws) return err;
   const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 8192);
   if (bf16_out)
     hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
+  else if (accumulate)
+    hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN,
+                       p.splits);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
   return hipGetLastError();

@@ -32,8 +32,9 @@ struct GemmPlan {
 // Deterministic launch plan of a GEMM shape (host only, no device access).
 GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K);
 
+// accumulate: out (fp32) = out + GEMM instead of out = GEMM.
 hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
-                    void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, void *ws,
+                    void *out, bool bf16_out, bool accumulate, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream);
 
 }  // namespace puro

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 3
+#define PURO_ABI_VERSION 4
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -200,6 +200,24 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode,
                                     int64_t M, int64_t N, int64_t K,
                                     void *workspace, size_t workspace_bytes,
                                     puro_stream_t stream);
+
+/*
+ * puro_gemm_fp8_blockwise_accumulate -- the same GEMM, added into an fp32
+ * output: out[m][n] = fp32(out[m][n] + G[m][n]), where G is exactly the value
+ * puro_gemm_fp8_blockwise computes with PURO_OUT_F32 (one fp32 addition per
+ * element).  For micro-batched training, whose weight gradients are summed
+ * over the micro-batches of a step into one fp32 buffer (the pages tune
+ * micro-batch sizes per pipeline stage: en.roboind.com article on Puro-2B,
+ * section "Unit cost, higher computing power").  Arguments as for
+ * puro_gemm_fp8_blockwise; out [M][N] fp32 is read and written and must not
+ * overlap any operand or the workspace.  K = 0 leaves out unchanged.
+ */
+puro_status puro_gemm_fp8_blockwise_accumulate(puro_gemm_mode mode,
+                                               const uint8_t *a, const float *sa,
+                                               const uint8_t *b, const float *sb,
+                                               float *out, int64_t M, int64_t N, int64_t K,
+                                               void *workspace, size_t workspace_bytes,
+                                               puro_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_str(puro_status s);

@@ -262,6 +262,16 @@ def gemm(mode: int, a, sa, b, sb) -> np.ndarray:
     return out
 
 
+def gemm_accumulate(mode: int, a, sa, b, sb, c) -> np.ndarray:
+    """The accumulating GEMM (micro-batched weight gradients summed into one fp32
+    buffer: the en.roboind.com article on Puro-2B tunes micro-batch sizes, section
+    "Unit cost, higher computing power"): c + gemm(...), both in fp64, c an fp32 [M][N]
+    array.  The kernels add in fp32, so they differ from this by that addition's
+    rounding (half an fp32 ulp of the sum) on top of the GEMM's own tolerance."""
+    c = np.asarray(c, dtype=np.float32)
+    return c.astype(np.float64) + gemm(mode, a, sa, b, sb)
+
+
 def gemm_at(mode: int, a, sa, b, sb, ms, ns) -> np.ndarray:
     """fp64 reference values at positions (ms[i], ns[i])."""
     a, sa, b, sb, M, N, K = _gemm_args(mode, a, sa, b, sb)

@@ -28,6 +28,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
                             "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
+                            "puro_gemm_fp8_blockwise_accumulate",
                             "puro_status_str", "puro_abi_version"])
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 3
+    assert puro.puro_abi_version() == 4
     for s in range(10):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -161,6 +162,28 @@ def test_gemm_validation():
     assert call(out=A0) == ALIAS
     assert call(out=A3) == ALIAS                          # out starts on sb
     if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
+        assert call() == DEVICE
+        assert call(K=0, a=None, sa=None, b=None, sb=None) == DEVICE
+
+
+def test_gemm_accumulate_validation():
+    f = puro.puro_gemm_fp8_blockwise_accumulate
+    M, N, K = 256, 256, 256
+    args = dict(a=A0, sa=A1, b=A2, sb=A3, out=A4)
+
+    def call(mode=0, M=M, N=N, K=K, ws=None, wsb=0, **kw):
+        a = dict(args, **kw)
+        return f(mode, a["a"], a["sa"], a["b"], a["sb"], a["out"], M, N, K, ws, wsb)
+
+    assert call(mode=3) == MODE
+    assert call(K=100) == SHAPE
+    assert call(M=0) == OK
+    assert call(out=None) == NULL
+    assert call(b=None) == NULL
+    assert call(out=A4 + 4) == ALIGN
+    assert call(out=A2 + 1024) == ALIAS                   # out inside b
+    assert call(mode=2, M=2048, N=2048, K=16384) == WS      # split-K plan needs a workspace
+    if no_gpu():
         assert call() == DEVICE
         assert call(K=0, a=None, sa=None, b=None, sb=None) == DEVICE
 

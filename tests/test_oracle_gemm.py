@@ -197,3 +197,26 @@ def test_bf16_rounding_single_rounding_from_fp64(orc):
     for h in (0x0001, 0x007F, 0x0080, 0x4049, 0x7F7F):
         val = float(Fraction(int(np.uint32(h << 16).view(np.float32).astype(np.float64) * 2 ** 140), 2 ** 140))
         assert orc.f64_to_bf16(val) == h
+
+
+@pytest.mark.parametrize("mode", [FPROP, WGRAD])
+def test_accumulate_integer_exact(orc, mode):
+    """Accumulating GEMM: integer codes, power-of-two scales and an integer-valued c, so
+    c + GEMM is exact in fp64 and must equal numpy's int64 arithmetic."""
+    M, N, K = 40, 72, 384
+    rng = np.random.default_rng(17 + mode)
+    a, sa, b, sb = random_operands(rng, mode, M, N, K, codes=int_codes(orc))
+    sa = np.ones_like(sa)
+    sb = np.ones_like(sb)
+    c = rng.integers(-1000, 1000, size=(M, N)).astype(np.float32)
+    got = orc.gemm_accumulate(mode, a, sa, b, sb, c)
+    ai = np.rint(torch_decode(a)).astype(np.int64)
+    bi = np.rint(torch_decode(b)).astype(np.int64)
+    assert np.array_equal(got, (ai @ bi.T + c.astype(np.int64)).astype(np.float64))
+
+
+def test_accumulate_onto_zero_is_the_gemm(orc):
+    rng = np.random.default_rng(23)
+    a, sa, b, sb = random_operands(rng, DGRAD, 64, 96, 256)
+    assert np.array_equal(orc.gemm_accumulate(DGRAD, a, sa, b, sb, np.zeros((64, 96), np.float32)),
+                          orc.gemm(DGRAD, a, sa, b, sb))
