@@ -23,6 +23,8 @@ Other workloads (--workload):
                    the bf16 X;
   requant          the requantizer alone over the layer's four saved inputs
                    (16384 x 2048 three times, 16384 x 6144): HBM GB/s;
+  layer_accum      the layer step of one micro-batch whose weight gradients are
+                   added into persistent fp32 buffers (accumulating wgrad);
   swiglu_quant     the fused SwiGLU + 1x128 / 128x1 quantization of the MLP's
                    gate/up output at 16384 tokens (16384 x 12288 in, the down
                    projection's two operands out): HBM GB/s;
@@ -66,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 30, or 300 for a single-kernel workload)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: 10, or 300 for a single-kernel workload)")
     ap.add_argument("--workload", default="layer",
-                    choices=["layer", "layer_fp8_saved", "requant", "swiglu_quant", "qkv_fprop", "mlp_fprop",
+                    choices=["layer", "layer_fp8_saved", "layer_accum", "requant", "swiglu_quant", "qkv_fprop", "mlp_fprop",
                              "mlp_down_bwd"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,23 +162,32 @@ def build_plan(workload, tensors, puro, torch):
                                bytes_=R * I * (4 + 2 * (1 + 4 / 128))))
         return (q, s), (qt, st)
 
-    def gemm(mode, a, b, out_dtype, name):
+    def gemm(mode, a, b, out_dtype, name, accumulate=False):
         (aq, sa), (bq, sb) = a, b
         M, K = aq.shape
         N = bq.shape[0]
         out = alloc((M, N), out_dtype)
+        if accumulate:
+            out.zero_()
         need = puro.puro_gemm_workspace_bytes(mode, M, N, K)
         ws = alloc((max(need, 16),), torch.uint8)
         od = puro.OUT_BF16 if out_dtype == torch.bfloat16 else puro.OUT_F32
-        args = (mode, aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), out.data_ptr(), od,
-                M, N, K, ws.data_ptr(), need, stream)
         flops = 2.0 * M * N * K
-        launches.append(Launch("gemm:" + ("wgrad" if mode == puro.WGRAD else "fprop_dgrad"), name,
-                               lambda: check(puro.puro_gemm_fp8_blockwise(*args), name), flops=flops,
-                               bytes_=M * K + N * K + 4 * M * cdiv(K, 128) + 4 * N * cdiv(K, 128) + M * N * (2 if od else 4)))
+        kind = "gemm:" + ("wgrad" if mode == puro.WGRAD else "fprop_dgrad") + ("_acc" if accumulate else "")
+        if accumulate:
+            args = (mode, aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), out.data_ptr(),
+                    M, N, K, ws.data_ptr(), need, stream)
+            fn = lambda: check(puro.puro_gemm_fp8_blockwise_accumulate(*args), name)
+        else:
+            args = (mode, aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), out.data_ptr(), od,
+                    M, N, K, ws.data_ptr(), need, stream)
+            fn = lambda: check(puro.puro_gemm_fp8_blockwise(*args), name)
+        launches.append(Launch(kind, name, fn, flops=flops,
+                               bytes_=M * K + N * K + 4 * M * cdiv(K, 128) + 4 * N * cdiv(K, 128)
+                               + M * N * (8 if accumulate else (2 if od else 4))))
         return out
 
-    if workload == "layer":
+    if workload in ("layer", "layer_accum"):
         from workloads import LINEARS
         for lin in LINEARS:
             x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
@@ -185,7 +196,7 @@ def build_plan(workload, tensors, puro, torch):
             dyrow, dyt = q_act_dual(dy, lin + ".quant_dy")
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
-            gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad")
+            gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad", accumulate=workload == "layer_accum")
     elif workload == "layer_fp8_saved":
         from workloads import LINEARS
         for lin in LINEARS:
@@ -229,6 +240,7 @@ def build_plan(workload, tensors, puro, torch):
 WORKLOAD_DESC = {
     "layer": ("Qwen3-1.7B-shaped layer (Puro-2B), 16384 tokens: QKV 2048->4096, O 2048->2048, "
               "gate_up 2048->12288, down 6144->2048; fprop+dgrad+wgrad and every quantize/transpose kernel"),
+    "layer_accum": ("the layer step (16384 tokens) of one micro-batch: wgrad adds into persistent fp32 dW buffers"),
     "layer_fp8_saved": ("the layer step (16384 tokens) with FP8-saved inputs: X quantized 1x128 only, the wgrad "
                         "operand X^T requantized from those codes"),
     "requant": ("requantization of the layer's saved 1x128 input codes into transposed 128x1 tiles, 16384 tokens: "
@@ -337,12 +349,10 @@ def cpu_baseline(tensors, workload, budget_s):
     import oracle
     from workloads import bits
     oracle.build(force=False)
-    if workload == "layer":
+    if workload in ("layer", "layer_accum", "layer_fp8_saved", "mlp_fprop"):
         x, w = tensors["x_gate_up"], tensors["w_gate_up"]
     elif workload == "qkv_fprop":
         x, w = tensors["x"], tensors["w"]
-    elif workload == "mlp_fprop":
-        x, w = tensors["x_gate_up"], tensors["w_gate_up"]
     else:
         x, w = tensors["dy"], tensors["w"].T.contiguous()
     xb, wb = bits(x), bits(w)
@@ -392,8 +402,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "swiglu_quant":
         tensors = workloads.make("mlp_swiglu", seed=args.seed, device="cuda")
-    elif args.workload in ("layer_fp8_saved", "requant"):
-        names = None if args.workload == "layer_fp8_saved" else {"x_" + lin for lin in workloads.LINEARS}
+    elif args.workload in ("layer_fp8_saved", "layer_accum", "requant"):
+        names = None if args.workload != "requant" else {"x_" + lin for lin in workloads.LINEARS}
         tensors = workloads.make("layer", seed=args.seed, device="cuda", names=names)
     else:
         tensors = workloads.make(args.workload, seed=args.seed, device="cuda")
