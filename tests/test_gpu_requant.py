@@ -58,6 +58,16 @@ def test_scales_at_the_bottom_of_the_normal_range(orc):
     check(orc, random_codes((R, C), 5), random_scales((cdiv(C, TILE), R), 6, log2_lo=-126.0, log2_hi=-112.0))
 
 
+def test_large_scales_take_the_division_path(orc):
+    """Column scales above 2^60 (saved scales of 2^64 .. 2^100) divide with IEEE division;
+    the middle tile column keeps ordinary scales and takes the fast path in the same launch."""
+    R, C = 256, 384
+    q = random_codes((R, C), 41)
+    s = random_scales((cdiv(C, TILE), R), 42, log2_lo=64.0, log2_hi=100.0)
+    s[1] = random_scales((R,), 43)
+    check(orc, q, s)
+
+
 def test_unit_scales_every_code_round_trips(orc):
     """Unit scales and a +-448 in every 128-row column tile: the result is the
     plain transpose of the codes, for every finite code byte."""
