@@ -9,11 +9,15 @@ The arithmetic lives in ``oracle.c`` (plain C99, fp64 for the GEMM); this file
 only builds it with gcc and marshals numpy arrays through ctypes.  What each
 function computes, and the passage it follows, is stated in ``oracle.c``.
 
+Functions: the e4m3 and bf16 scalars, the tile quantizers (1x128, 128x128,
+128x1 and transposed 128x128), the requantizer of saved 1x128 codes, SwiGLU
+of the gate/up output, and the fp64 GEMM (full, sampled, accumulating).
+
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 (exhaustive e4m3 agreement with PyTorch's CPU cast, code round-trips, tile
 invariants, hand-derived golden tiles, integer-exact GEMMs, linearity in
 power-of-two scales, a library fp64 matmul cross-check, brute force on tiny
-inputs).
+inputs, 50-digit arithmetic for SwiGLU).
 """
 from __future__ import annotations
 

@@ -23,14 +23,20 @@
  *   - GEMM: out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k], where deq multiplies
  *     a decoded code by its tile scale.  Computed here in fp64.
  *   - a tile that runs past the end of a row (a ragged tail) covers only the
- *     elements that exist.
+ *     elements that exist;
+ *   - requantization of saved 1x128 codes (orc_requant_act_t): dequantize to
+ *     fp32 with one rounding, then the 128x1 rule on the transpose;
+ *   - SwiGLU of the MLP's gate/up output (orc_swiglu): bf16 of the fp64 value
+ *     of silu(g) * u, gate in the first half of each row.
  *
  * Parity pins (independent checks of this file) live in the test-suite:
  * exhaustive agreement of the encoder with PyTorch's CPU float8_e4m3fn cast,
  * code round-trips, the tile invariants (|q| <= 448, all-zero tile -> scale 1,
  * exactly representable tiles round-trip, power-of-two equivariance), hand
  * derived golden tiles, integer-exact GEMMs against numpy int64, linearity of
- * the GEMM in power-of-two scales and a numpy fp64 cross-check.
+ * the GEMM in power-of-two scales and a numpy fp64 cross-check; for the
+ * requantizer a torch composition, reduction to the bf16 transposed
+ * quantizer and closed forms; for SwiGLU 50-digit arithmetic.
  *
  * Plain C99 + OpenMP (loops over independent tiles / output rows only).
  * Build without fast-math and without FP contraction.
