@@ -139,12 +139,48 @@ def _bf16_input(x: torch.Tensor, name: str):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _tensor(t, name: str, dtype, shape, device=None):
+    """The C calls take raw pointers and cannot check sizes: every tensor handed to them
+    through these helpers is checked here (CUDA, dtype, exact shape, contiguous, device)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    return t
+
+
+def _gemm_operands(mode: int, a, sa, b, sb):
+    if mode not in (FPROP, DGRAD, WGRAD):
+        raise ValueError("unknown GEMM mode %r" % (mode,))
+    if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
+        raise TypeError("a and b must be 2-D tensors")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b must share K")
+    dev = a.device
+    nk = _cdiv(K, TILE)
+    _tensor(a, "a", torch.uint8, (M, K))
+    _tensor(b, "b", torch.uint8, (N, K), dev)
+    _tensor(sa, "sa", torch.float32, (nk, M), dev)
+    _tensor(sb, "sb", torch.float32, (nk, N) if mode == WGRAD else (_cdiv(N, TILE), nk), dev)
+    return M, N, K, dev
+
+
 def quant_act_1x128(x: torch.Tensor, q=None, s=None, stream=None):
     """1x128 tiles: returns (q uint8 [R][C], s fp32 [ceil(C/128)][R])."""
     _bf16_input(x, "x")
     R, C = x.shape
     q = torch.empty((R, C), dtype=torch.uint8, device=x.device) if q is None else q
     s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device) if s is None else s
+    _tensor(q, "q", torch.uint8, (R, C), x.device)
+    _tensor(s, "s", torch.float32, (_cdiv(C, TILE), R), x.device)
     _check(puro_quant_act_1x128(x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
            "puro_quant_act_1x128")
     return q, s
@@ -156,6 +192,8 @@ def quant_w_128x128(w: torch.Tensor, q=None, s=None, stream=None):
     R, C = w.shape
     q = torch.empty((R, C), dtype=torch.uint8, device=w.device) if q is None else q
     s = torch.empty((_cdiv(R, TILE), _cdiv(C, TILE)), dtype=torch.float32, device=w.device) if s is None else s
+    _tensor(q, "q", torch.uint8, (R, C), w.device)
+    _tensor(s, "s", torch.float32, (_cdiv(R, TILE), _cdiv(C, TILE)), w.device)
     _check(puro_quant_w_128x128(w.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
            "puro_quant_w_128x128")
     return q, s
@@ -190,13 +228,15 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
 def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=None):
     """Saved 1x128 codes q uint8 [R][C] and scales s fp32 [ceil(C/128)][R] ->
     (qt uint8 [C][R], st fp32 [ceil(R/128)][C]) in transposed 128x1 tiles."""
-    if q.dtype != torch.uint8 or q.dim() != 2 or not q.is_cuda or not q.is_contiguous():
-        raise TypeError("q must be a contiguous 2-D uint8 CUDA tensor")
+    if not isinstance(q, torch.Tensor) or q.dim() != 2:
+        raise TypeError("q must be a 2-D tensor")
     R, C = q.shape
-    if s.dtype != torch.float32 or tuple(s.shape) != (_cdiv(C, TILE), R) or not s.is_contiguous():
-        raise ValueError("s must be a contiguous fp32 tensor of shape [ceil(C/128)][R]")
+    _tensor(q, "q", torch.uint8, (R, C))
+    _tensor(s, "s", torch.float32, (_cdiv(C, TILE), R), q.device)
     qt = torch.empty((C, R), dtype=torch.uint8, device=q.device) if qt is None else qt
     st = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device) if st is None else st
+    _tensor(qt, "qt", torch.uint8, (C, R), q.device)
+    _tensor(st, "st", torch.float32, (_cdiv(R, TILE), C), q.device)
     _check(puro_requant_act_t(q.data_ptr(), s.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
                               _stream(stream)), "puro_requant_act_t")
     return qt, st
@@ -237,19 +277,20 @@ def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):
 
 def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=None, workspace=None,
                        stream=None):
-    """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K:
-        raise ValueError("a and b must share K")
+    """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes.
+    sa [ceil(K/128)][M]; sb [ceil(N/128)][ceil(K/128)] (FPROP, DGRAD) or [ceil(K/128)][N] (WGRAD)."""
+    M, N, K, dev = _gemm_operands(mode, a, sa, b, sb)
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+        out = torch.empty((M, N), dtype=out_dtype, device=dev)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
+    _tensor(out, "out", out.dtype, (M, N), dev)
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     need = puro_gemm_workspace_bytes(mode, M, N, K)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev):
+        raise ValueError("workspace must be a contiguous CUDA tensor on %s" % dev)
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(puro_gemm_fp8_blockwise(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
@@ -259,16 +300,15 @@ def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=No
 
 
 def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, workspace=None, stream=None):
-    """out (fp32 [M][N]) += the blockwise-scaled FP8 GEMM of a [M][K] and b [N][K]; returns out."""
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K:
-        raise ValueError("a and b must share K")
-    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous fp32 tensor of shape [M][N]")
+    """out (fp32 [M][N]) += the blockwise-scaled FP8 GEMM of a [M][K] and b [N][K]; returns out.
+    Scale layouts as for gemm_fp8_blockwise."""
+    M, N, K, dev = _gemm_operands(mode, a, sa, b, sb)
+    _tensor(out, "out", torch.float32, (M, N), dev)
     need = puro_gemm_workspace_bytes(mode, M, N, K)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=a.device)
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev):
+        raise ValueError("workspace must be a contiguous CUDA tensor on %s" % dev)
     wptr = workspace.data_ptr() if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(puro_gemm_fp8_blockwise_accumulate(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),

@@ -213,3 +213,18 @@ def test_gemm_workspace_errors():
     assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A4 + 16, need) == ALIAS
     if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
         assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5, need) == DEVICE
+
+
+def test_tensor_helpers_reject_host_tensors_and_bad_modes():
+    """The tensor helpers check their tensors before any C call (they need CUDA tensors)."""
+    import torch
+    a = torch.zeros((16, 128), dtype=torch.uint8)
+    sa = torch.zeros((1, 16), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        puro.gemm_fp8_blockwise(puro.FPROP, a, sa, a, torch.zeros((1, 1)))
+    with pytest.raises(ValueError):
+        puro.gemm_fp8_blockwise(7, a, sa, a, torch.zeros((1, 1)))
+    with pytest.raises(TypeError):
+        puro.requant_act_t(a, sa)
+    with pytest.raises(TypeError):
+        puro.quant_act_1x128(torch.zeros((16, 128), dtype=torch.bfloat16))

@@ -235,3 +235,21 @@ def test_mfma_slice_accumulation_precision(orc):
         print("%s: max |err| / sum|products| = %.3g (2^%.1f)" % (name, worst[name], np.log2(max(worst[name], 1e-300))))
     assert max(worst.values()) < 2.0 ** -10
     assert worst["normal"] < 2.0 ** -14
+
+
+def test_helpers_reject_wrong_scale_layouts(orc):
+    """Scale tensors of the wrong layout for the mode are refused before the C call
+    (the kernels would read past them)."""
+    a, sa, b, sb = quantized_operands(orc, WGRAD, 256, 256, 256, seed=1)
+    A, SA, B, SB = (torch.from_numpy(x).cuda() for x in (a, sa, b, sb))
+    with pytest.raises(ValueError):
+        puro.gemm_fp8_blockwise(FPROP, A, SA, B, SB)                  # row-scaled sb given to a block-scaled mode
+    with pytest.raises(ValueError):
+        puro.gemm_fp8_blockwise(WGRAD, A, SA[:, :128].contiguous(), B, SB)
+    with pytest.raises(TypeError):
+        puro.gemm_fp8_blockwise(WGRAD, A, SA.double(), B, SB)
+    with pytest.raises(ValueError):
+        puro.gemm_fp8_blockwise_accumulate(WGRAD, A, SA, B, SB, torch.zeros((256, 128), device="cuda"))
+    out = puro.gemm_fp8_blockwise(WGRAD, A, SA, B, SB, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert out.shape == (256, 256)
