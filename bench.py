@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: 10, or 300 for a single-kernel workload)")
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "layer_fp8_saved", "layer_accum", "requant", "swiglu_quant", "qkv_fprop", "mlp_fprop",
-                             "mlp_down_bwd"])
+                             "mlp_down_bwd", "mlp_swiglu_fprop", "mlp_swiglu_fused", "mlp_swiglu_fused_nogu"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -152,15 +152,35 @@ def build_plan(workload, tensors, puro, torch):
                                bytes_=R * C * (2 + 4 / 128 + 4 / 128)))
         return qt, st
 
-    def swiglu(gu, name):
+    def swiglu(gu, name, dual=True):
         R, C2 = gu.shape
         I = C2 // 2
         q, s = alloc((R, I), torch.uint8), alloc((cdiv(I, 128), R), torch.float32)
-        qt, st = alloc((I, R), torch.uint8), alloc((cdiv(R, 128), I), torch.float32)
-        args = (gu.data_ptr(), R, I, q.data_ptr(), s.data_ptr(), qt.data_ptr(), st.data_ptr(), None, stream)
+        qt = st = None
+        if dual:
+            qt, st = alloc((I, R), torch.uint8), alloc((cdiv(R, 128), I), torch.float32)
+        args = (gu.data_ptr(), R, I, q.data_ptr(), s.data_ptr(), qt.data_ptr() if dual else None,
+                st.data_ptr() if dual else None, None, stream)
         launches.append(Launch("swiglu_quant", name, lambda: check(puro.puro_swiglu_quant(*args), name),
-                               bytes_=R * I * (4 + 2 * (1 + 4 / 128))))
+                               bytes_=R * I * (4 + (2 if dual else 1) * (1 + 4 / 128))))
         return (q, s), (qt, st)
+
+    def gemm_swiglu(a, b, name, write_gu=True):
+        """gate_up fprop with the SwiGLU quantizer as its epilogue; writes gu (for the backward) too
+        unless write_gu is false."""
+        (aq, sa), (bq, sb) = a, b
+        M, K = aq.shape
+        N = bq.shape[0]
+        I = N // 2
+        gu = alloc((M, N), torch.bfloat16) if write_gu else None
+        q, s = alloc((M, I), torch.uint8), alloc((I // 128, M), torch.float32)
+        args = (aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), M, I, K,
+                gu.data_ptr() if write_gu else None, q.data_ptr(), s.data_ptr(), stream)
+        launches.append(Launch("gemm:fprop_swiglu", name, lambda: check(puro.puro_gemm_fp8_swiglu_quant(*args), name),
+                               flops=2.0 * M * N * K,
+                               bytes_=M * K + N * K + 4 * (M + N // 128) * cdiv(K, 128) + (M * N * 2 if write_gu else 0)
+                               + M * I * (1 + 4 / 128)))
+        return q, s
 
     def gemm(mode, a, b, out_dtype, name, accumulate=False):
         (aq, sa), (bq, sb) = a, b
@@ -228,6 +248,16 @@ def build_plan(workload, tensors, puro, torch):
             xrow = q_act(tensors["x_" + lin], lin + ".quant_x")
             wrow, _ = q_w_dual(tensors["w_" + lin], lin + ".quant_w", transposed=False)
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
+    elif workload in ("mlp_swiglu_fprop", "mlp_swiglu_fused", "mlp_swiglu_fused_nogu"):
+        xrow = q_act(tensors["x_gate_up"], "gate_up.quant_x")
+        wgu, _ = q_w_dual(tensors["w_gate_up"], "gate_up.quant_w", transposed=False)
+        wdn, _ = q_w_dual(tensors["w_down"], "down.quant_w", transposed=False)
+        if workload != "mlp_swiglu_fprop":
+            h = gemm_swiglu(xrow, wgu, "gate_up.fprop_swiglu_quant", write_gu=workload == "mlp_swiglu_fused")
+        else:
+            gu = gemm(puro.FPROP, xrow, wgu, torch.bfloat16, "gate_up.fprop")
+            h, _ = swiglu(gu, "down.swiglu_quant", dual=False)
+        gemm(puro.FPROP, h, wdn, torch.bfloat16, "down.fprop")
     elif workload == "mlp_down_bwd":
         dyrow, dyt = q_act_dual(tensors["dy"], "quant_dy")
         _, wt = q_w_dual(tensors["w"], "quant_w")
@@ -250,6 +280,12 @@ WORKLOAD_DESC = {
     "qkv_fprop": "QKV projection fprop, 4096 tokens: X[4096x2048] x W[4096x2048]^T -> bf16",
     "mlp_fprop": "MLP fprop, 8192 tokens: gate_up X[8192x2048] x W[12288x2048]^T, down X[8192x6144] x W[2048x6144]^T",
     "mlp_down_bwd": "MLP down backward, 8192 tokens: dgrad dY[8192x2048] x W[2048x6144], wgrad dY^T x X[8192x6144]",
+    "mlp_swiglu_fprop": ("MLP forward, 16384 tokens: gate_up fprop X[16384x2048] x W[12288x2048]^T -> bf16, SwiGLU "
+                         "quantizer -> 1x128 codes of h [16384x6144], down fprop h x W[2048x6144]^T"),
+    "mlp_swiglu_fused": ("MLP forward, 16384 tokens, as mlp_swiglu_fprop with the SwiGLU quantizer fused into the "
+                         "gate_up GEMM's epilogue (the bf16 gate/up output is still written for the backward)"),
+    "mlp_swiglu_fused_nogu": ("MLP forward, 16384 tokens, as mlp_swiglu_fused without writing the bf16 gate/up "
+                              "output (a backward that recomputes it)"),
 }
 
 
@@ -349,7 +385,8 @@ def cpu_baseline(tensors, workload, budget_s):
     import oracle
     from workloads import bits
     oracle.build(force=False)
-    if workload in ("layer", "layer_accum", "layer_fp8_saved", "mlp_fprop"):
+    if workload in ("layer", "layer_accum", "layer_fp8_saved", "mlp_fprop", "mlp_swiglu_fprop", "mlp_swiglu_fused",
+                    "mlp_swiglu_fused_nogu"):
         x, w = tensors["x_gate_up"], tensors["w_gate_up"]
     elif workload == "qkv_fprop":
         x, w = tensors["x"], tensors["w"]
@@ -402,6 +439,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "swiglu_quant":
         tensors = workloads.make("mlp_swiglu", seed=args.seed, device="cuda")
+    elif args.workload in ("mlp_swiglu_fused", "mlp_swiglu_fused_nogu"):
+        tensors = workloads.make("mlp_swiglu_fprop", seed=args.seed, device="cuda")
     elif args.workload in ("layer_fp8_saved", "layer_accum", "requant"):
         names = None if args.workload != "requant" else {"x_" + lin for lin in workloads.LINEARS}
         tensors = workloads.make("layer", seed=args.seed, device="cuda", names=names)

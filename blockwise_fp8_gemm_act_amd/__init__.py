@@ -8,11 +8,13 @@ importing this package fails.
 
 The raw C calls keep their C names (``puro_quant_act_1x128``,
 ``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_requant_act_t``,
-``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_accumulate``, ...) and take
-integer device pointers.  The
+``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_accumulate``,
+``puro_gemm_fp8_swiglu_quant``, ...) and take integer device pointers.  The
 tensor-level helpers ``quant_act_1x128``, ``quant_w_128x128``,
-``quant_transpose``, ``requant_act_t``, ``gemm_fp8_blockwise`` allocate
-outputs with torch and call them on the current stream.
+``quant_transpose``, ``requant_act_t``, ``swiglu_quant``,
+``gemm_fp8_blockwise``, ``gemm_fp8_blockwise_accumulate`` and
+``gemm_fp8_swiglu_quant`` allocate outputs with torch and call them on the
+current stream.
 """
 from __future__ import annotations
 
@@ -58,6 +60,8 @@ _lib.puro_gemm_fp8_blockwise.restype = ctypes.c_int
 _lib.puro_gemm_fp8_blockwise_accumulate.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P,
                                                     _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
 _lib.puro_gemm_fp8_blockwise_accumulate.restype = ctypes.c_int
+_lib.puro_gemm_fp8_swiglu_quant.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]
+_lib.puro_gemm_fp8_swiglu_quant.restype = ctypes.c_int
 _lib.puro_status_str.argtypes = [ctypes.c_int]
 _lib.puro_status_str.restype = ctypes.c_char_p
 _lib.puro_abi_version.argtypes = []
@@ -106,6 +110,10 @@ def puro_gemm_fp8_blockwise_accumulate(mode, a, sa, b, sb, out, M, N, K, workspa
                                        stream=None) -> int:
     return _lib.puro_gemm_fp8_blockwise_accumulate(mode, a, sa, b, sb, out, M, N, K, workspace,
                                                    workspace_bytes, stream)
+
+
+def puro_gemm_fp8_swiglu_quant(a, sa, b, sb, M, inter, K, gu, hq, hs, stream=None) -> int:
+    return _lib.puro_gemm_fp8_swiglu_quant(a, sa, b, sb, M, inter, K, gu, hq, hs, stream)
 
 
 def puro_status_str(status: int) -> str:
@@ -315,3 +323,21 @@ def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, wo
                                               out.data_ptr(), M, N, K, wptr, wbytes, _stream(stream)),
            "puro_gemm_fp8_blockwise_accumulate")
     return out
+
+
+def gemm_fp8_swiglu_quant(a, sa, b, sb, write_gu: bool = True, stream=None):
+    """Fprop of a fused gate/up projection with the SwiGLU quantizer as its epilogue.
+    a [M][K] codes, sa [ceil(K/128)][M]; b [2I][K] codes (gate rows, then up rows),
+    sb [2I/128][ceil(K/128)].  Returns (hq uint8 [M][I], hs fp32 [I/128][M], gu), gu being
+    the bf16 gate/up output [M][2I] (None unless write_gu)."""
+    M, N, K, dev = _gemm_operands(FPROP, a, sa, b, sb)
+    if N % (2 * TILE):
+        raise ValueError("b must have 2*I rows with I a multiple of 128")
+    I = N // 2
+    hq = torch.empty((M, I), dtype=torch.uint8, device=dev)
+    hs = torch.empty((I // TILE, M), dtype=torch.float32, device=dev)
+    gu = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if write_gu else None
+    _check(puro_gemm_fp8_swiglu_quant(a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(), M, I, K,
+                                      gu.data_ptr() if write_gu else None, hq.data_ptr(), hs.data_ptr(),
+                                      _stream(stream)), "puro_gemm_fp8_swiglu_quant")
+    return hq, hs, gu

@@ -247,6 +247,27 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const
   return gemm_call(mode, a, sa, b, sb, out, out_dtype, false, M, N, K, workspace, workspace_bytes, stream);
 }
 
+puro_status puro_gemm_fp8_swiglu_quant(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                                       int64_t M, int64_t inter, int64_t K, uint16_t *gu, uint8_t *hq, float *hs,
+                                       puro_stream_t stream) {
+  if (inter < 0 || inter > kMaxDim / 2 || inter % 128 != 0) return PURO_ERR_SHAPE;
+  if (!shape_ok(M, K) || !shape_ok(2 * inter, K) || !shape_ok(M, 2 * inter) || K % 16 != 0 || K > kMaxGemmK)
+    return PURO_ERR_SHAPE;
+  if ((inter + 16) * K >= (int64_t(1) << 32)) return PURO_ERR_SHAPE;      // B row offsets in 32 bits
+  if (cdiv(M, 256) * (inter / 128) > kMaxDim) return PURO_ERR_SHAPE;
+  if (M == 0 || inter == 0) return PURO_OK;
+  if (!hq || !hs) return PURO_ERR_NULL;
+  if (K > 0 && (!a || !sa || !b || !sb)) return PURO_ERR_NULL;
+  if (!aligned16(hq) || !aligned16(hs) || (gu && !aligned16(gu))) return PURO_ERR_ALIGN;
+  if (K > 0 && (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb))) return PURO_ERR_ALIGN;
+  const int64_t nk = cdiv(K, 128);
+  const Range in[] = {rng(a, M * K), rng(sa, nk * M * 4), rng(b, 2 * inter * K), rng(sb, 2 * inter / 128 * nk * 4)};
+  const Range outs[] = {rng(gu, gu ? M * 2 * inter * 2 : 0), rng(hq, M * inter), rng(hs, inter / 128 * M * 4)};
+  if (any_alias(in, K > 0 ? 4 : 0, outs, 3)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_gemm_swiglu_quant(a, sa, b, sb, gu, hq, hs, M, inter, K, (hipStream_t)stream));
+}
+
 puro_status puro_gemm_fp8_blockwise_accumulate(puro_gemm_mode mode, const uint8_t *a, const float *sa,
                                                const uint8_t *b, const float *sb, float *out,
                                                int64_t M, int64_t N, int64_t K,

@@ -1,5 +1,5 @@
 // Device helpers shared by the gfx950 kernels: bf16 unpacking, the e4m3 tile
-// scale and code rule, DPP reductions.
+// scale and code rule, DPP reductions, the SwiGLU value.
 //
 // Quantization rule (the pages name DeepSeek-V3's fine-grained block
 // quantization for the main linear layers -- en.roboind.com article on
@@ -132,6 +132,44 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// SwiGLU of one gate/up pair, h = bf16(silu(g) * u), silu(g) = g / (1 + e^-g).
+// The value is defined as the fp64 evaluation of that expression, rounded
+// once to bf16 (round to nearest even).
+//
+// Fast path, fp32: s = g * rcp(1 + expf(-g)) is within 2.94 * 2^-24 of
+// silu(g) (relative) for every bf16 g with |g| <= 64, measured exhaustively
+// on gfx950 against fp64; with the rounding of p = s * u, p is within 3.44
+// fp32 ulps of the exact product.  So unless p's low 16 bits lie within 5
+// ulps of the bf16 rounding midpoint (0x8000), rounding p gives the bf16 of
+// the exact value, which the fp64 value rounds to as well.  Otherwise, or for
+// |g| > 64, the element takes the fp64 evaluation (swiglu_f64).
+__device__ __forceinline__ uint32_t swiglu_fast(float g, float u, bool &slow) {
+  const float e = expf(-g);
+  const float sg = g * __builtin_amdgcn_rcpf(1.0f + e);
+  const float p = sg * u;
+  const uint32_t b = __float_as_uint(p);
+  slow = ((b & 0xffffu) - 0x7ffbu) <= 10u || !(__builtin_fabsf(g) <= 64.0f);
+  return (b + 0x8000u) >> 16;
+}
+
+// bf16 bits of v, round to nearest even (from fp64: one rounding).
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double v) {
+  const uint32_t sign = signbit(v) ? 0x8000u : 0u;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (a < 0x1p-126) return sign | (uint32_t)rint(ldexp(a, 133));   // 2^-133 grid
+  int e = ilogb(a);
+  double n = rint(ldexp(a, 7 - e));                                 // 128 .. 256
+  if (n == 256.0) { n = 128.0; ++e; }
+  if (e > 127) return sign | 0x7f80u;
+  return sign | ((uint32_t)(e + 127) << 7) | ((uint32_t)n - 128u);
+}
+
+__device__ __forceinline__ uint32_t swiglu_f64(float g, float u) {
+  const double gd = g, ud = u;
+  return f64_to_bf16_bits(gd / (1.0 + exp(-gd)) * ud);
 }
 
 }  // namespace puro

@@ -33,9 +33,10 @@
 //    bank-conflict free;
 //  - rows past M or N are read from clamped (valid) rows and never stored;
 //    K chunks past K read a 16-byte zero page, so a ragged last slice adds 0;
-//  - an item's slices are promoted in a fixed order that depends on the item
-//    alone (a rotation by (item % 8) / 8 of its K range, which keeps the
-//    items that share an XCD's L2 in lockstep and staggers the 8 XCDs);
+//  - an item's slices are promoted in a fixed order that depends on its row
+//    tile alone (a rotation by (tm % 8) / 8 of its K range, which keeps the
+//    items that share an XCD's L2 in lockstep and staggers the 8 XCDs), so
+//    every output element sees the same order whatever the column tiling;
 //    optional split-K writes fp32 partials to a workspace that a second
 //    kernel sums in a fixed order.  Results are deterministic;
 //  - accumulate mode (fp32 out): out = fp32(out + GEMM), one addition of the
@@ -72,6 +73,11 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int splits;      // K-loop splits (1: no workspace)
   int spl;         // slices per split
+  // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
+  // out is the optional bf16 gate/up output [M][2I]
+  int64_t I;
+  uint8_t *hq;     // codes of h [M][I]
+  float *hs;       // their 1x128 scales [I/128][M]
 };
 
 
@@ -158,6 +164,44 @@ __device__ __forceinline__ void dma_slice8(const void *abase, const void *bbase,
       : "memory", "scc");
 }
 
+// The same 8 copies with separate lane offsets for B (its rows do not follow
+// A's row pattern in the fused SwiGLU kernel).
+__device__ __forceinline__ void dma_slice8ab(const void *abase, const void *bbase, uint32_t a0, uint32_t a1,
+                                             uint32_t a2, uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,
+                                             uint32_t b3, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %11\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %9\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %5, %10\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %9\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %6, %10\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %9\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %7, %10\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %9\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %8, %10\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "v"(b0), "v"(b1), "v"(b2), "v"(b3), "s"(abase), "s"(bbase), "s"(lds)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -172,7 +216,8 @@ struct Tile {
   int split;
 };
 
-__device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item) {
+// glu: the tile covers h columns n0 .. n0+127 (B rows: 128 gate + 128 up rows).
+__device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = false) {
   const int total_tiles = g.tiles_m * g.tiles_n;
   Tile t;
   t.split = item / total_tiles;
@@ -180,16 +225,19 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item) {
   const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
   const int tn = tile / g.tiles_m;
   t.m0 = tm * kBM;
-  t.n0 = tn * kBN;
+  t.n0 = tn * (glu ? kBK : kBN);
   t.kb_begin = t.split * g.spl;
   t.kb_end = min(g.nk, t.kb_begin + g.spl);
   // Items that run on one XCD at the same time (item = b + rG, workgroup b on
-  // XCD b % 8, G a multiple of 8) share item % 8 and so walk K in lockstep,
-  // sharing their A and B panels through that XCD's L2; the 8 XCDs start
-  // 1/8 of the K range apart.  The order depends on the item alone.
-  t.rot = (int)(((unsigned)(item & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
+  // XCD b % 8, G a multiple of 8) share item % 8, which is tm % 8 when the
+  // row-tile count is a multiple of 8: they walk K in lockstep, sharing their
+  // A and B panels through that XCD's L2, and the 8 XCDs start 1/8 of the K
+  // range apart.  The order depends on the row tile alone, so an output
+  // element is summed in the same order by the plain fprop and by the fused
+  // SwiGLU kernel (whose column tiles differ).
+  t.rot = (int)(((unsigned)(tm & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
   t.rows_a = min((int)g.M - t.m0, kBM);
-  t.rows_b = min((int)g.N - t.n0, kBN);
+  t.rows_b = glu ? kBN : min((int)g.N - t.n0, kBN);
   return t;
 }
 
@@ -206,12 +254,14 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 // slices as one stream: the first slice of the next item is copied while the
 // last slice of the current one is computed, and the current item's output
 // leaves with direct global stores that drain while the next item computes.
-template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false>
+template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(!kAcc || (!kBf16Out && !kToWs), "accumulate mode stores fp32 directly");
+  static_assert(!kGlu || (!kRowScaledB && kBf16Out && !kToWs && !kAcc), "the SwiGLU epilogue follows an fprop");
   // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
   __shared__ __align__(1024) uint8_t smem[2][2][kSliceBytes];
   __shared__ __align__(16) float sscale[2][2][kBM];
+  __shared__ __align__(16) uint32_t xamax[kGlu ? 2 * kBM : 1];   // SwiGLU: row maxima of |h| per half tile
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -268,6 +318,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       const float *src = g.sb + (int64_t)kb * g.N + tl.n0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, tl.rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+    } else if constexpr (kGlu) {
+      // lane 0 brings the scale of the tile's gate block, lane 1 that of its up block
+      const float *src = g.sb + (int64_t)(tl.n0 / kBK) * g.nk + kb;
+      dma4_s(src, (uint32_t)(ln == 1 ? g.I / kBK : 0) * (uint32_t)g.nk * 4, ls + kBM * 4);
     } else {
       // lane l brings sb[n-block nb0 + l][kb] (clamped); lanes 0 and 1 cover
       // the tile's two 128-column blocks
@@ -278,14 +332,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
   };
 
+  // Fused SwiGLU: tile row r of B (r = 8j + i, i < 8) is gate row n0 + 4j + i
+  // for i < 4 and up row I + n0 + 4j + i - 4 otherwise, so that n-blocks 2p
+  // and 2p+1 give each lane the gate and up values of the same 4 h columns.
+  auto glu_brow = [&](int r) -> int64_t {
+    const int i = r & 7;
+    return (int64_t)(4 * (r >> 3)) + (i < 4 ? i : g.I + i - 4);
+  };
   auto issue_slice = [&](const Tile &tl, int kb, int buf) {
     const int kofs = kb * kBK;
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const uint8_t *a_tile = g.a + (int64_t)tl.m0 * g.K;
     const uint8_t *b_tile = g.b + (int64_t)tl.n0 * g.K;
     if (tl.rows_a == kBM && tl.rows_b == kBN && !(ktail && kb == g.nk - 1)) {
-      dma_slice8(a_tile + (int64_t)(w * 32) * g.K + kofs, b_tile + (int64_t)(w * 32) * g.K + kofs, voff0,
-                 voff1, voff2, voff3, la + w * 4096);
+      if constexpr (kGlu) {
+        // the wave's row groups 4w .. 4w+3 start at gate row n0 + 16w
+        int ln = __lane_id();
+        asm volatile("" : "+v"(ln));
+        const uint32_t rb = (uint32_t)glu_brow(ln >> 3) * (uint32_t)K;
+        dma_slice8ab(a_tile + (int64_t)(w * 32) * g.K + kofs, b_tile + (int64_t)(w * 16) * g.K + kofs, voff0, voff1,
+                     voff2, voff3, rb + (uint32_t)dma_chunk(ln, 0), rb + (uint32_t)(4 * K + dma_chunk(ln, 1)),
+                     rb + (uint32_t)(8 * K + dma_chunk(ln, 2)), rb + (uint32_t)(12 * K + dma_chunk(ln, 3)),
+                     la + w * 4096);
+      } else {
+        dma_slice8(a_tile + (int64_t)(w * 32) * g.K + kofs, b_tile + (int64_t)(w * 32) * g.K + kofs, voff0,
+                   voff1, voff2, voff3, la + w * 4096);
+      }
     } else {
       // edge tiles and the ragged last slice: chunks at or past K read a zero page
       const uint32_t lb = la + kSliceBytes;
@@ -299,7 +371,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         const int kc = dma_chunk(ln, j);
         const bool kin = kofs + kc < K;
         const uint8_t *pa = kin ? a_tile + kofs + (r < tl.rows_a ? (int64_t)r * K : 0) + kc : g_zero16;
-        const uint8_t *pb = kin ? b_tile + kofs + (r < tl.rows_b ? (int64_t)r * K : 0) + kc : g_zero16;
+        const int64_t br = kGlu ? glu_brow(r) : (r < tl.rows_b ? (int64_t)r : 0);
+        const uint8_t *pb = kin ? b_tile + kofs + br * K + kc : g_zero16;
         dma16_v(pa, la + grp * 1024);
         dma16_v(pb, lb + grp * 1024);
       }
@@ -359,13 +432,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   float sa[4];               // row scale sA of the lane's row in each m-block
   v4f sbn0 = {1.f, 1.f, 1.f, 1.f};   // row-scaled B: column scales of the coming slice's n-block 0
   float sbk = 1.0f;          // block-scaled B: the coming slice's scale of the wave's 128 columns
+  float sbu = 1.0f;          // fused SwiGLU: sbk is the gate block's scale, sbu the up block's
   auto load_scales = [&](int buf) {
     const float *lsa = sscale[buf][0];
     const float *lsb = sscale[buf][1];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) sa[mb] = lsa[wm * 64 + mb * 16 + fr];
     if constexpr (kRowScaledB) sbn0 = *reinterpret_cast<const v4f *>(&lsb[wn * 128 + colB(0)]);
-    else sbk = lsb[wn];
+    else if constexpr (kGlu) {
+      sbk = lsb[0];
+      sbu = lsb[1];
+    } else sbk = lsb[wn];
   };
 
   // One slice from buffer `buf`.  Step nb issues the 4 MFMAs of n-block nb;
@@ -382,6 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     v4f sbv[8];                // row-scaled B: column scales of each n-block
     sbv[0] = sbn0;
     float sc[4];               // block-scaled B: promotion factors sA * sB
+    float scu[4];              // fused SwiGLU: those of the up n-blocks (odd nb)
     // the buffer of the previous slice was released by the barrier inside it
     if constexpr (kNext) issue_slice(nxt, kb_next, buf ^ 1);
     auto promote = [&](int pb, int mb) {
@@ -390,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         const v4f ps = P[mb] * sbv[pb];                          // column scale first, in place
         acc[mb][pb] = __builtin_elementwise_fma(ps, (v4f)sa[mb], prev);
       } else {
-        acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)sc[mb], prev);
+        acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)((kGlu && (pb & 1)) ? scu[mb] : sc[mb]), prev);
       }
     };
 #pragma unroll
@@ -414,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
             bf[nb & 1], af[mb], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
         if (nb == 7 && kPre) af[mb] = load_fragA(smem[buf ^ 1][0], mb);
         if (nb == 0 && !kRowScaledB) sc[mb] = sa[mb] * sbk;
+        if (nb == 0 && kGlu) scu[mb] = sa[mb] * sbu;
       }
       // issue order within the step: LDS reads first (a whole step to land),
       // then VALU groups between the MFMAs
@@ -424,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-          if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // VALU
+          if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, kGlu ? 2 : 1, 0);  // VALU
         }
       } else if (nb < 7) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);
@@ -454,7 +533,122 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // for m-block mb and n-block pair p, row m0 + wm*64 + 16mb + fr at the 8
   // columns n0 + wn*128 + 32p + 8q .. +7 (n-block 2p: the first 4, 2p+1: the
   // last 4): one 16-byte store of bf16, two of fp32.
+  // Fused SwiGLU epilogue.  Lane (q, fr) holds, for m-block mb and pair p,
+  // row m0 + wm*64 + 16mb + fr at h columns n0 + wn*64 + 16p + 4q .. +3: the
+  // gate values in acc[mb][2p] and the up values in acc[mb][2p+1].  Both are
+  // rounded to bf16 (the gate/up output), h = SwiGLU(g, u) in bf16, and each
+  // row's 128 h columns (this wave's 64 and the partner wave's, wn ^ 1) form
+  // one 1x128 tile: scale from the tile's max |h|, codes h / s.
+  auto glu_store = [&](const Tile &tl) {
+    const int hc = tl.n0 + wn * 64 + 4 * q;
+    typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    auto pk2 = [](float a, float b) -> uint32_t {     // the bf16 output's conversion (RNE)
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+    };
+    u32x2 gp[4][4], up[4][4], hp[4][4];   // packed bf16 gate, up and h of (mb, p)
+    uint64_t slow = 0;                    // bit 16mb + 4p + e: element e of (mb, p) needs fp64
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const v4f ga = acc[mb][2 * p], ua = acc[mb][2 * p + 1];
+        gp[mb][p] = (u32x2){pk2(ga[0], ga[1]), pk2(ga[2], ga[3])};
+        up[mb][p] = (u32x2){pk2(ua[0], ua[1]), pk2(ua[2], ua[3])};
+        uint32_t hb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t gw = gp[mb][p][e >> 1], uw = up[mb][p][e >> 1];
+          bool sl;
+          hb[e] = swiglu_fast((e & 1) ? bf16hi(gw) : bf16lo(gw), (e & 1) ? bf16hi(uw) : bf16lo(uw), sl);
+          slow |= (uint64_t)sl << (16 * mb + 4 * p + e);
+        }
+        hp[mb][p] = (u32x2){(hb[0] & 0xffffu) | hb[1] << 16, (hb[2] & 0xffffu) | hb[3] << 16};
+      }
+    if (g.out != nullptr) {
+      uint16_t *gu = reinterpret_cast<uint16_t *>(g.out);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+        if (m >= g.M) continue;
+        uint16_t *row = gu + (int64_t)m * 2 * g.I + hc;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          *reinterpret_cast<u32x2 *>(row + 16 * p) = gp[mb][p];
+          *reinterpret_cast<u32x2 *>(row + g.I + 16 * p) = up[mb][p];
+        }
+      }
+    }
+    // rare elements near a bf16 rounding midpoint, or with |g| > 64: fp64,
+    // one element per iteration, picked out of the packed words by selects
+    while (slow) {
+      const int i = __builtin_ctzll(slow);
+      slow &= slow - 1;
+      const int wi = i >> 1;
+      uint32_t gw = 0, uw = 0;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const bool hit = wi == (4 * mb + p) * 2 + hh;
+            gw = hit ? gp[mb][p][hh] : gw;
+            uw = hit ? up[mb][p][hh] : uw;
+          }
+      const bool odd = i & 1;
+      const uint32_t h = swiglu_f64(odd ? bf16hi(gw) : bf16lo(gw), odd ? bf16hi(uw) : bf16lo(uw));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t w0 = hp[mb][p][hh];
+            const uint32_t merged = odd ? ((w0 & 0xffffu) | (h << 16)) : ((w0 & 0xffff0000u) | h);
+            hp[mb][p][hh] = wi == (4 * mb + p) * 2 + hh ? merged : w0;
+          }
+    }
+    // row maxima of |h|: the lane's 16 values, the 4 lanes q of the row, then
+    // the partner wave through LDS
+    uint32_t am[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      uint32_t mx = 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t w0 = hp[mb][p][hh];
+          mx = max(mx, max(w0 & 0x7fffu, (w0 >> 16) & 0x7fffu));
+        }
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16));
+      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32));
+      am[mb] = mx;
+      if (q == 0) xamax[wn * kBM + wm * 64 + mb * 16 + fr] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+      const TileQ tq = make_tileq(mag_to_float(max(am[mb], xamax[(wn ^ 1) * kBM + wm * 64 + mb * 16 + fr])));
+      if (m >= g.M) continue;
+      uint8_t *row = g.hq + (int64_t)m * g.I + hc;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x2 w0 = hp[mb][p];
+        *reinterpret_cast<uint32_t *>(row + 16 * p) =
+            pack4_e4m3(quot(bf16lo(w0.x), tq), quot(bf16hi(w0.x), tq), quot(bf16lo(w0.y), tq), quot(bf16hi(w0.y), tq));
+      }
+      if (wn == 0 && q == 0) g.hs[(int64_t)(tl.n0 / kBK) * g.M + m] = tq.s;
+    }
+  };
+
   auto store_item = [&](const Tile &tl) {
+    if constexpr (kGlu) {
+      glu_store(tl);
+      return;
+    }
     const int64_t wbase = (int64_t)(tl.m0 + wm * 64) * g.N + tl.n0 + wn * 128;
     const int64_t loff = (int64_t)fr * g.N + 8 * q;
     typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -533,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
   };
 
-  Tile cur = tile_of(g, item);
+  Tile cur = tile_of(g, item, kGlu);
   issue_slice(cur, kb_at(cur, 0), 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -565,10 +759,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     // final-slice variant costs the register allocator its accumulators).
     const int next_item = item + (int)gridDim.x;
     const bool more = next_item < total_items;
-    const Tile nxt = tile_of(g, more ? next_item : item);
-    slice(buf, nxt, kb_at(nxt, 0), std::true_type{}, std::true_type{}, std::false_type{});
+    const Tile nxt = tile_of(g, more ? next_item : item, kGlu);
+    // (the SwiGLU epilogue needs the registers of the next item's fragments:
+    // those are read after it)
+    slice(buf, nxt, kb_at(nxt, 0), std::true_type{}, std::bool_constant<!kGlu>{}, std::false_type{});
     buf ^= 1;
     store_item(cur);
+    if constexpr (kGlu) {
+      bf[0] = load_fragB(smem[buf][1], 0);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) af[mb] = load_fragA(smem[buf][0], mb);
+      load_scales(buf);
+    }
     if (!more) break;
     item = next_item;
     cur = nxt;
@@ -602,6 +804,11 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(void *out, int64_t MN) {
     else
       reinterpret_cast<float *>(out)[i] = 0.0f;
   }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
 }
 
 // ---------------------------------------------------------------- planning
@@ -701,6 +908,37 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
                        p.splits);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
+  return hipGetLastError();
+}
+
+// Fused gate/up fprop + SwiGLU + 1x128 quantizer.  One work item per 256
+// rows x 128 h columns (its 128 gate and 128 up rows of B); no split-K.  The
+// results are those of the bf16 fprop followed by the SwiGLU quantizer.
+hipError_t run_gemm_swiglu_quant(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                                 uint16_t *gu, uint8_t *hq, float *hs, int64_t M, int64_t I, int64_t K,
+                                 hipStream_t stream) {
+  if (M == 0 || I == 0) return hipSuccess;
+  if (K == 0) {
+    // g = u = 0: h = 0, every tile scale 1, codes +0
+    auto fill = [&](void *p, int64_t words, uint32_t v) {
+      const int blocks = (int)std::min<int64_t>((words + 255) / 256, 65536);
+      hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, stream, (uint32_t *)p, words, v);
+    };
+    if (gu) fill(gu, M * I, 0u);
+    fill(hq, M * I / 4, 0u);
+    fill(hs, I / kBK * M, 0x3f800000u);
+    return hipGetLastError();
+  }
+  GemmArgs g{};
+  g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.out = gu; g.ws = nullptr;
+  g.M = M; g.N = 2 * I; g.K = K;
+  g.nk = (int)((K + kBK - 1) / kBK);
+  g.tiles_m = (int)((M + kBM - 1) / kBM);
+  g.tiles_n = (int)(I / kBK);
+  g.splits = 1; g.spl = g.nk;
+  g.I = I; g.hq = hq; g.hs = hs;
+  const dim3 grid((unsigned)std::min<int64_t>((int64_t)g.tiles_m * g.tiles_n, compute_units()));
+  hipLaunchKernelGGL((gemm_fp8_bw_kernel<false, true, false, false, true>), grid, dim3(kThreads), 0, stream, g);
   return hipGetLastError();
 }
 

@@ -37,4 +37,11 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
                     void *out, bool bf16_out, bool accumulate, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream);
 
+// Fused fprop of a gate/up projection (B = [gate rows; up rows], 2I x K,
+// 128x128 block scales) with the SwiGLU quantizer as its epilogue: gu (bf16
+// [M][2I], optional), hq / hs (1x128 codes and scales of h).  I % 128 == 0.
+hipError_t run_gemm_swiglu_quant(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                                 uint16_t *gu, uint8_t *hq, float *hs, int64_t M, int64_t I, int64_t K,
+                                 hipStream_t stream);
+
 }  // namespace puro

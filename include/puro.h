@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 4
+#define PURO_ABI_VERSION 5
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -218,6 +218,36 @@ puro_status puro_gemm_fp8_blockwise_accumulate(puro_gemm_mode mode,
                                                float *out, int64_t M, int64_t N, int64_t K,
                                                void *workspace, size_t workspace_bytes,
                                                puro_stream_t stream);
+
+/*
+ * puro_gemm_fp8_swiglu_quant -- the fprop of the MLP's fused gate/up
+ * projection with puro_swiglu_quant as its epilogue: the down projection's
+ * 1x128 FP8 input is written straight from the GEMM's accumulators (the
+ * SwiGLU MLP and the FP8 main linears as in puro_swiglu_quant; the 1x128
+ * rule of puro_quant_act_1x128).  hq and hs are bit for bit what
+ *   puro_swiglu_quant(gu, M, inter, hq, hs, NULL, NULL, NULL)
+ * makes of this call's own gu, without gu passing through memory on the way
+ * to h; gu is bit for bit what
+ *   puro_gemm_fp8_blockwise(PURO_FPROP, a, sa, b, sb, gu, PURO_OUT_BF16, M, 2*inter, K)
+ * writes whenever that call needs no workspace (no split of its K loop, as
+ * for every layer shape at 16384 tokens), and within the same tolerance of
+ * the exact product otherwise (the split sums in another order).
+ *   a    [M][K] uint8 codes, sa [ceil(K/128)][M] fp32 (1x128 activation codes)
+ *   b    [2*inter][K] uint8 codes, sb [2*inter/128][ceil(K/128)] fp32 (128x128
+ *        weight codes): gate rows first, then up rows
+ *   gu   (optional, NULL to skip) [M][2*inter] bf16: the gate/up output that
+ *        the fprop alone would write (the SwiGLU backward needs it)
+ *   hq   [M][inter] uint8, hs [inter/128][M] fp32: 1x128 codes and scales of
+ *        h = bf16(silu(g) u) (output)
+ * inter must be a multiple of 128 and K of 16, with (inter + 16) * K < 2^32;
+ * M is free.  K = 0 gives g = u = 0: h = 0, codes 0, scales 1.  No workspace
+ * (no split of the K loop).  The result is deterministic for a given shape.
+ */
+puro_status puro_gemm_fp8_swiglu_quant(const uint8_t *a, const float *sa,
+                                       const uint8_t *b, const float *sb,
+                                       int64_t M, int64_t inter, int64_t K,
+                                       uint16_t *gu, uint8_t *hq, float *hs,
+                                       puro_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *puro_status_str(puro_status s);

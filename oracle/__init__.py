@@ -11,7 +11,8 @@ function computes, and the passage it follows, is stated in ``oracle.c``.
 
 Functions: the e4m3 and bf16 scalars, the tile quantizers (1x128, 128x128,
 128x1 and transposed 128x128), the requantizer of saved 1x128 codes, SwiGLU
-of the gate/up output, and the fp64 GEMM (full, sampled, accumulating).
+of the gate/up output, and the fp64 GEMM (full, sampled, accumulating, and
+followed by the SwiGLU quantizer).
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 (exhaustive e4m3 agreement with PyTorch's CPU cast, code round-trips, tile
@@ -240,6 +241,26 @@ def swiglu_quant(gu: np.ndarray, dual: bool = False):
 
 
 # ---------------------------------------------------------------- GEMM
+def gemm_swiglu_quant(a, sa, b, sb, rows=None):
+    """Fprop of a fused gate/up projection followed by the SwiGLU quantizer: the
+    down projection's FP8 input made straight from the gate/up GEMM (the pages put
+    the main linears on the FP8 path: en.roboind.com article on Puro-2B, section
+    "FP8 takes advantage of the RTX 5090's low precision efficiency").
+      gu = bf16(gemm(FPROP, a, sa, b, sb))   one rounding of each fp64 value
+      (h, q, s) = swiglu_quant(gu)           b's first half of rows is the gate
+    rows: optional row indices; the result then covers a[rows] only (rows of the
+    product are independent).  Returns (gu, h, q, s)."""
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    sa = np.ascontiguousarray(sa, dtype=np.float32)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        a = np.ascontiguousarray(a[rows])
+        sa = np.ascontiguousarray(sa[:, rows])
+    gu = f64_to_bf16_array(gemm(FPROP, a, sa, b, sb))
+    h, q, s = swiglu_quant(gu)
+    return gu, h, q, s
+
+
 def _gemm_args(mode, a, sa, b, sb):
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)

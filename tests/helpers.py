@@ -43,22 +43,26 @@ def bf16_ordered(h: np.ndarray) -> np.ndarray:
 
 def check_gemm_values(out: np.ndarray, ref: np.ndarray, na: np.ndarray, nb: np.ndarray,
                       bf16: bool, orc, what: str):
-    """out/ref/na/nb aligned arrays (full matrices or samples).
+    """out/ref/na/nb aligned arrays (full matrices or samples); a bf16 output is
+    passed as its uint16 bit patterns.
 
     fp32 output: normalized error <= 1e-4 everywhere.
     bf16 output: within 1 bf16 ulp of the oracle's bf16 rounding of its fp64
     value, or (near-cancellation elements) normalized error <= 1e-4.
     Returns (max normalized error, fraction strictly within 1 ulp)."""
     denom = na * nb
-    err = np.abs(out.astype(np.float64) - ref)
+    if bf16:
+        assert out.dtype == np.uint16, "bf16 outputs are compared as their bit patterns"
+        vals = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        vals = out.astype(np.float64)
+    err = np.abs(vals - ref)
     norm = np.where(denom > 0, err / np.where(denom > 0, denom, 1), np.where(err == 0, 0.0, np.inf))
     worst = float(norm.max()) if norm.size else 0.0
     strict = 1.0
     if bf16:
         ref16 = orc.f64_to_bf16_array(ref)
-        got16 = out.view(np.uint16) if out.dtype == np.uint16 else None
-        assert got16 is not None
-        ulps = np.abs(bf16_ordered(got16) - bf16_ordered(ref16))
+        ulps = np.abs(bf16_ordered(out) - bf16_ordered(ref16))
         ok = (ulps <= 1) | (norm <= GEMM_TOL)
         strict = float(np.mean(ulps <= 1)) if ulps.size else 1.0
         assert ok.all(), "%s: %d elements beyond 1 ulp and tolerance; worst norm err %.3g" % (

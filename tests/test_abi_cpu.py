@@ -28,7 +28,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
                             "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
-                            "puro_gemm_fp8_blockwise_accumulate",
+                            "puro_gemm_fp8_blockwise_accumulate", "puro_gemm_fp8_swiglu_quant",
                             "puro_status_str", "puro_abi_version"])
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 4
+    assert puro.puro_abi_version() == 5
     for s in range(10):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -185,6 +185,39 @@ def test_gemm_accumulate_validation():
     assert call(mode=2, M=2048, N=2048, K=16384) == WS      # split-K plan needs a workspace
     if no_gpu():
         assert call() == DEVICE
+        assert call(K=0, a=None, sa=None, b=None, sb=None) == DEVICE
+
+
+def test_gemm_swiglu_quant_validation():
+    f = puro.puro_gemm_fp8_swiglu_quant
+    M, I, K = 256, 256, 256
+    args = dict(a=A0, sa=A1, b=A2, sb=A3, gu=A4, hq=A5, hs=A6)
+
+    def call(M=M, I=I, K=K, **kw):
+        a = dict(args, **kw)
+        return f(a["a"], a["sa"], a["b"], a["sb"], M, I, K, a["gu"], a["hq"], a["hs"])
+
+    assert call(I=192) == SHAPE                            # inter must be a multiple of 128
+    assert call(I=-128) == SHAPE
+    assert call(K=100) == SHAPE
+    assert call(M=-1) == SHAPE
+    assert call(K=1 << 24) == SHAPE
+    assert call(I=1 << 30, K=16) == SHAPE                  # 2 * inter over the dimension limit
+    assert call(I=1 << 22, K=1024) == SHAPE                # B row offsets past 32 bits
+    assert call(M=0) == OK and call(I=0) == OK
+    assert call(hq=None) == NULL
+    assert call(hs=None) == NULL
+    assert call(a=None) == NULL
+    assert call(sb=None) == NULL
+    assert call(a=A0 + 1) == ALIGN
+    assert call(gu=A4 + 2) == ALIGN
+    assert call(hs=A6 + 4) == ALIGN
+    assert call(hq=A2 + 4096) == ALIAS                     # hq inside b
+    assert call(hs=A4 + 1024) == ALIAS                     # hs inside gu
+    assert call(gu=A5) == ALIAS                            # gu starts on hq
+    if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
+        assert call() == DEVICE
+        assert call(gu=None) == DEVICE
         assert call(K=0, a=None, sa=None, b=None, sb=None) == DEVICE
 
 

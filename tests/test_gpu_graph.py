@@ -1,7 +1,8 @@
 """The C calls enqueue kernels only (no allocation, no memset, no host wait), so
 a caller can capture them in a HIP graph.  One linear's forward and backward
 operands, its three GEMMs (a split-K wgrad among them), the accumulating
-wgrad, the requantizer and the fused SwiGLU are captured once and replayed
+wgrad, the requantizer, the fused SwiGLU and the gate/up fprop with the SwiGLU
+epilogue are captured once and replayed
 several times, with eager work between the replays; every replay must give
 the eager results bit for bit."""
 import numpy as np
@@ -41,6 +42,8 @@ class Buffers:
         self.dx = e((T, K), torch.bfloat16)
         self.dw = e((N, K), f32)
         self.dw_acc = e((N, K), f32)
+        self.gu2 = e((T, N), torch.bfloat16)                  # W read as a gate/up weight of inter N / 2
+        self.fq, self.fs = e((T, N // 2)), e((N // 256, T), f32)
         need = max(puro.puro_gemm_workspace_bytes(m, *s) for m, s in
                    ((puro.FPROP, (T, N, K)), (puro.DGRAD, (T, K, N)), (puro.WGRAD, (N, K, T))))
         self.work = e((max(need, 16),))
@@ -49,7 +52,7 @@ class Buffers:
     def outputs(self):
         return [self.xq, self.xs, self.xqt, self.xst, self.wq, self.ws_, self.wqt, self.wst, self.dq, self.ds,
                 self.dqt, self.dst, self.rqt, self.rst, self.hq, self.hs, self.hqt, self.hst, self.y, self.dx,
-                self.dw, self.dw_acc]
+                self.dw, self.dw_acc, self.gu2, self.fq, self.fs]
 
     def enqueue(self):
         st = torch.cuda.current_stream().cuda_stream
@@ -69,6 +72,8 @@ class Buffers:
                                         puro.OUT_F32, N, K, T, p(self.work), self.need, st))
         ok(puro.puro_gemm_fp8_blockwise_accumulate(puro.WGRAD, p(self.dqt), p(self.dst), p(self.rqt), p(self.rst),
                                                    p(self.dw_acc), N, K, T, p(self.work), self.need, st))
+        ok(puro.puro_gemm_fp8_swiglu_quant(p(self.xq), p(self.xs), p(self.wq), p(self.ws_), T, N // 2, K,
+                                           p(self.gu2), p(self.fq), p(self.fs), st))
 
 
 def snapshot(buf):

@@ -119,6 +119,10 @@ WORKLOADS = {
     # The MLP's gate/up projection output at 16384 tokens (gate then up, 2 x 6144
     # columns): the input of the SwiGLU that feeds the down projection.
     "mlp_swiglu": [Spec("gu", (16384, 2 * INTER), "act", outliers=0)],
+    # The MLP forward at 16384 tokens with the SwiGLU quantizer between its two
+    # projections (gate_up X [16384x2048] x W [12288x2048]^T, down W [2048x6144]).
+    "mlp_swiglu_fprop": [_act("x_gate_up", 16384, HIDDEN), _w("w_gate_up", 2 * INTER, HIDDEN),
+                         _w("w_down", HIDDEN, INTER)],
     # One whole layer's four linears at 16384 tokens, forward and backward.
     "layer": [t for lin, (kin, kout) in LINEARS.items() for t in (
         _act(f"x_{lin}", 16384, kin), _w(f"w_{lin}", kout, kin),
