@@ -43,7 +43,14 @@
 //    finished GEMM value per element, in the store epilogue or, with split-K,
 //    in the reduction.  It lets micro-batches add their weight gradients into
 //    one fp32 buffer (the pages tune micro-batch sizes per pipeline stage:
-//    en.roboind.com article, section "Unit cost, higher computing power").
+//    en.roboind.com article, section "Unit cost, higher computing power");
+//  - SwiGLU mode (fprop of a fused gate/up weight, bf16 out): a tile covers
+//    128 h columns, i.e. 128 gate and 128 up rows of B interleaved in groups
+//    of 4, and the epilogue writes the 1x128 codes and scales of
+//    h = bf16(silu(g) * u) -- the down projection's FP8 input -- with the
+//    bf16 gate/up output optional.  The epilogue runs after the item's last
+//    slice and does not overlap MFMA work, which makes it cost more than the
+//    separate SwiGLU quantizer pass unless the gate/up output is dropped.
 #include "device_common.h"
 #include "launch.h"
 
