@@ -289,11 +289,21 @@ WORKLOAD_DESC = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank space, so that edits to comments do not
+    count as kernel changes (the sources hold no comment markers inside string literals)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(family="gemm"):
+    """Hash of the code (comments and spacing aside) of the kernel sources a traffic record was taken on."""
     h = hashlib.sha256()
     for p in TRAFFIC[family][1]:
-        with open(p, "rb") as fh:
-            h.update(fh.read())
+        with open(p) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
