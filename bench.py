@@ -69,7 +69,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default: 10, or 300 for a single-kernel workload)")
     ap.add_argument("--workload", default="layer",
                     choices=["layer", "layer_fp8_saved", "layer_accum", "requant", "swiglu_quant", "qkv_fprop", "mlp_fprop",
-                             "mlp_down_bwd", "mlp_swiglu_fprop", "mlp_swiglu_fused", "mlp_swiglu_fused_nogu"])
+                             "mlp_down_bwd", "mlp_swiglu_fprop", "mlp_swiglu_fused", "mlp_swiglu_fused_nogu", "layer_tm"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -120,6 +120,16 @@ def build_plan(workload, tensors, puro, torch):
         launches.append(Launch("quant", name, lambda: check(puro.puro_quant_transpose(*args), name),
                                bytes_=R * C * (2 + 2 * (1 + 4 / 128))))
         return (q, s), (qt, st)
+
+    def q_act_tm(x, name):
+        """1x128 codes and the 128x1 codes in x's own layout (token-major wgrad operand), one read."""
+        R, C = x.shape
+        qc, sc = alloc((R, C), torch.uint8), alloc((cdiv(R, 128), C), torch.float32)
+        q, s = alloc((R, C), torch.uint8), alloc((cdiv(C, 128), R), torch.float32)
+        args = (x.data_ptr(), R, C, qc.data_ptr(), sc.data_ptr(), q.data_ptr(), s.data_ptr(), stream)
+        launches.append(Launch("quant", name, lambda: check(puro.puro_quant_act_128x1(*args), name),
+                               bytes_=R * C * (2 + 2 * (1 + 4 / 128))))
+        return (q, s), (qc, sc)
 
     def q_act(x, name):
         R, C = x.shape
@@ -184,8 +194,12 @@ def build_plan(workload, tensors, puro, torch):
 
     def gemm(mode, a, b, out_dtype, name, accumulate=False):
         (aq, sa), (bq, sb) = a, b
-        M, K = aq.shape
-        N = bq.shape[0]
+        if mode == 3:                               # token-major wgrad operands: a [K][M], b [K][N]
+            K, M = aq.shape
+            N = bq.shape[1]
+        else:
+            M, K = aq.shape
+            N = bq.shape[0]
         out = alloc((M, N), out_dtype)
         if accumulate:
             out.zero_()
@@ -193,7 +207,7 @@ def build_plan(workload, tensors, puro, torch):
         ws = alloc((max(need, 16),), torch.uint8)
         od = puro.OUT_BF16 if out_dtype == torch.bfloat16 else puro.OUT_F32
         flops = 2.0 * M * N * K
-        kind = "gemm:" + ("wgrad" if mode == puro.WGRAD else "fprop_dgrad") + ("_acc" if accumulate else "")
+        kind = "gemm:" + {puro.WGRAD: "wgrad", 3: "wgrad_tm"}.get(mode, "fprop_dgrad") + ("_acc" if accumulate else "")
         if accumulate:
             args = (mode, aq.data_ptr(), sa.data_ptr(), bq.data_ptr(), sb.data_ptr(), out.data_ptr(),
                     M, N, K, ws.data_ptr(), need, stream)
@@ -217,6 +231,16 @@ def build_plan(workload, tensors, puro, torch):
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
             gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad", accumulate=workload == "layer_accum")
+    elif workload == "layer_tm":
+        from workloads import LINEARS
+        for lin in LINEARS:
+            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            xrow, xc = q_act_tm(x, lin + ".quant_x")
+            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            dyrow, dyc = q_act_tm(dy, lin + ".quant_dy")
+            gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
+            gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
+            gemm(3, dyc, xc, torch.float32, lin + ".wgrad")
     elif workload == "layer_fp8_saved":
         from workloads import LINEARS
         for lin in LINEARS:
@@ -271,6 +295,8 @@ WORKLOAD_DESC = {
     "layer": ("Qwen3-1.7B-shaped layer (Puro-2B), 16384 tokens: QKV 2048->4096, O 2048->2048, "
               "gate_up 2048->12288, down 6144->2048; fprop+dgrad+wgrad and every quantize/transpose kernel"),
     "layer_accum": ("the layer step (16384 tokens) of one micro-batch: wgrad adds into persistent fp32 dW buffers"),
+    "layer_tm": ("the layer step (16384 tokens) with token-major wgrad operands: X and dY quantized 1x128 and 128x1 "
+                 "in one read with the 128x1 codes untransposed, wgrad reading them token-major"),
     "layer_fp8_saved": ("the layer step (16384 tokens) with FP8-saved inputs: X quantized 1x128 only, the wgrad "
                         "operand X^T requantized from those codes"),
     "requant": ("requantization of the layer's saved 1x128 input codes into transposed 128x1 tiles, 16384 tokens: "
@@ -395,8 +421,8 @@ def cpu_baseline(tensors, workload, budget_s):
     import oracle
     from workloads import bits
     oracle.build(force=False)
-    if workload in ("layer", "layer_accum", "layer_fp8_saved", "mlp_fprop", "mlp_swiglu_fprop", "mlp_swiglu_fused",
-                    "mlp_swiglu_fused_nogu"):
+    if workload in ("layer", "layer_accum", "layer_fp8_saved", "layer_tm", "mlp_fprop", "mlp_swiglu_fprop",
+                    "mlp_swiglu_fused", "mlp_swiglu_fused_nogu"):
         x, w = tensors["x_gate_up"], tensors["w_gate_up"]
     elif workload == "qkv_fprop":
         x, w = tensors["x"], tensors["w"]
@@ -451,7 +477,7 @@ def main():
         tensors = workloads.make("mlp_swiglu", seed=args.seed, device="cuda")
     elif args.workload in ("mlp_swiglu_fused", "mlp_swiglu_fused_nogu"):
         tensors = workloads.make("mlp_swiglu_fprop", seed=args.seed, device="cuda")
-    elif args.workload in ("layer_fp8_saved", "layer_accum", "requant"):
+    elif args.workload in ("layer_fp8_saved", "layer_accum", "requant", "layer_tm"):
         names = None if args.workload != "requant" else {"x_" + lin for lin in workloads.LINEARS}
         tensors = workloads.make("layer", seed=args.seed, device="cuda", names=names)
     else:

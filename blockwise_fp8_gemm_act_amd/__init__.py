@@ -30,7 +30,7 @@ PURO_OK = 0
 STATUS_NAMES = {0: "PURO_OK", 1: "PURO_ERR_NULL", 2: "PURO_ERR_SHAPE", 3: "PURO_ERR_ALIGN",
                 4: "PURO_ERR_MODE", 5: "PURO_ERR_DTYPE", 6: "PURO_ERR_WORKSPACE",
                 7: "PURO_ERR_DEVICE", 8: "PURO_ERR_LAUNCH", 9: "PURO_ERR_ALIAS"}
-FPROP, DGRAD, WGRAD = 0, 1, 2
+FPROP, DGRAD, WGRAD, WGRAD_TM = 0, 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 T_ACT, T_WEIGHT = 0, 1
 TILE = 128
@@ -48,6 +48,8 @@ _lib.puro_quant_w_128x128.argtypes = [_P, _I64, _I64, _P, _P, _P]
 _lib.puro_quant_w_128x128.restype = ctypes.c_int
 _lib.puro_quant_transpose.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.puro_quant_transpose.restype = ctypes.c_int
+_lib.puro_quant_act_128x1.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P]
+_lib.puro_quant_act_128x1.restype = ctypes.c_int
 _lib.puro_requant_act_t.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
 _lib.puro_swiglu_quant.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]
 _lib.puro_swiglu_quant.restype = ctypes.c_int
@@ -86,6 +88,10 @@ def puro_quant_w_128x128(w, rows, cols, q, s, stream=None) -> int:
 
 def puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream=None) -> int:
     return _lib.puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream)
+
+
+def puro_quant_act_128x1(x, rows, cols, qc, sc, q_row, s_row, stream=None) -> int:
+    return _lib.puro_quant_act_128x1(x, rows, cols, qc, sc, q_row, s_row, stream)
 
 
 def puro_requant_act_t(q, s, rows, cols, qt, st, stream=None) -> int:
@@ -164,20 +170,26 @@ def _tensor(t, name: str, dtype, shape, device=None):
 
 
 def _gemm_operands(mode: int, a, sa, b, sb):
-    if mode not in (FPROP, DGRAD, WGRAD):
+    if mode not in (FPROP, DGRAD, WGRAD, WGRAD_TM):
         raise ValueError("unknown GEMM mode %r" % (mode,))
     if not isinstance(a, torch.Tensor) or a.dim() != 2 or not isinstance(b, torch.Tensor) or b.dim() != 2:
         raise TypeError("a and b must be 2-D tensors")
-    M, K = a.shape
-    N = b.shape[0]
-    if b.shape[1] != K:
-        raise ValueError("a and b must share K")
+    if mode == WGRAD_TM:              # token-major: a [K][M], b [K][N]
+        K, M = a.shape
+        N = b.shape[1]
+        if b.shape[0] != K:
+            raise ValueError("a and b must share K (their first dimension)")
+    else:
+        M, K = a.shape
+        N = b.shape[0]
+        if b.shape[1] != K:
+            raise ValueError("a and b must share K")
     dev = a.device
     nk = _cdiv(K, TILE)
-    _tensor(a, "a", torch.uint8, (M, K))
-    _tensor(b, "b", torch.uint8, (N, K), dev)
+    _tensor(a, "a", torch.uint8, tuple(a.shape))
+    _tensor(b, "b", torch.uint8, tuple(b.shape), dev)
     _tensor(sa, "sa", torch.float32, (nk, M), dev)
-    _tensor(sb, "sb", torch.float32, (nk, N) if mode == WGRAD else (_cdiv(N, TILE), nk), dev)
+    _tensor(sb, "sb", torch.float32, (nk, N) if mode in (WGRAD, WGRAD_TM) else (_cdiv(N, TILE), nk), dev)
     return M, N, K, dev
 
 
@@ -233,6 +245,24 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
     return (qt, st, q, s) if dual else (qt, st)
 
 
+def quant_act_128x1(x: torch.Tensor, dual: bool = False, stream=None):
+    """128x1 tiles with the codes in x's own layout: returns (qc uint8 [R][C], sc fp32
+    [ceil(R/128)][C]), plus (q, s) as quant_act_1x128 when dual."""
+    _bf16_input(x, "x")
+    R, C = x.shape
+    dev = x.device
+    qc = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    sc = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
+    q = s = None
+    if dual:
+        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
+        s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=dev)
+    _check(puro_quant_act_128x1(x.data_ptr(), R, C, qc.data_ptr(), sc.data_ptr(),
+                                q.data_ptr() if dual else None, s.data_ptr() if dual else None, _stream(stream)),
+           "puro_quant_act_128x1")
+    return (qc, sc, q, s) if dual else (qc, sc)
+
+
 def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=None):
     """Saved 1x128 codes q uint8 [R][C] and scales s fp32 [ceil(C/128)][R] ->
     (qt uint8 [C][R], st fp32 [ceil(R/128)][C]) in transposed 128x1 tiles."""
@@ -285,8 +315,9 @@ def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):
 
 def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=None, workspace=None,
                        stream=None):
-    """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes.
-    sa [ceil(K/128)][M]; sb [ceil(N/128)][ceil(K/128)] (FPROP, DGRAD) or [ceil(K/128)][N] (WGRAD)."""
+    """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes
+    (WGRAD_TM: a [K][M], b [K][N], token-major).  sa [ceil(K/128)][M]; sb [ceil(N/128)][ceil(K/128)]
+    (FPROP, DGRAD) or [ceil(K/128)][N] (WGRAD, WGRAD_TM)."""
     M, N, K, dev = _gemm_operands(mode, a, sa, b, sb)
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=dev)

@@ -160,6 +160,23 @@ puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t ro
   return launched(puro::run_quant_t_w(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
 }
 
+puro_status puro_quant_act_128x1(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qc, float *sc,
+                                 uint8_t *q_row, float *s_row, puro_stream_t stream) {
+  if (!shape_ok(rows, cols) || cols % 16 != 0) return PURO_ERR_SHAPE;
+  if ((q_row == nullptr) != (s_row == nullptr)) return PURO_ERR_NULL;
+  if (rows == 0 || cols == 0) return PURO_OK;
+  if (!x || !qc || !sc) return PURO_ERR_NULL;
+  const bool dual = q_row != nullptr;
+  if (!aligned16(x) || !aligned16(qc) || !aligned16(sc)) return PURO_ERR_ALIGN;
+  if (dual && (!aligned16(q_row) || !aligned16(s_row))) return PURO_ERR_ALIGN;
+  const Range in[] = {rng(x, rows * cols * 2)};
+  const Range out[] = {rng(qc, rows * cols), rng(sc, cdiv(rows, 128) * cols * 4),
+                       rng(q_row, dual ? rows * cols : 0), rng(s_row, dual ? cdiv(cols, 128) * rows * 4 : 0)};
+  if (any_alias(in, 1, out, 4)) return PURO_ERR_ALIAS;
+  if (puro_status d = check_device()) return d;
+  return launched(puro::run_quant_act_128x1(x, rows, cols, qc, sc, q_row, s_row, (hipStream_t)stream));
+}
+
 puro_status puro_swiglu_quant(const uint16_t *gu, int64_t rows, int64_t inter, uint8_t *q, float *s,
                               uint8_t *qt, float *st, uint16_t *h, puro_stream_t stream) {
   if (inter > kMaxDim / 2 || !shape_ok(rows, 2 * inter) || inter % 16 != 0) return PURO_ERR_SHAPE;
@@ -194,7 +211,7 @@ puro_status puro_requant_act_t(const uint8_t *q, const float *s, int64_t rows, i
 }
 
 size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int64_t K) {
-  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return 0;
+  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD && mode != PURO_WGRAD_TM) return 0;
   if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxGemmK) return 0;
   return puro::plan_gemm((int)mode, M, N, K).ws_bytes;
 }
@@ -206,10 +223,12 @@ namespace {
 puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                       void *out, puro_out_dtype out_dtype, bool accumulate, int64_t M, int64_t N, int64_t K,
                       void *workspace, size_t workspace_bytes, puro_stream_t stream) {
-  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD) return PURO_ERR_MODE;
+  if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD && mode != PURO_WGRAD_TM) return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_F32 && out_dtype != PURO_OUT_BF16) return PURO_ERR_DTYPE;
   if (!shape_ok(M, K) || !shape_ok(N, K) || !shape_ok(M, N) || K % 16 != 0 || K > kMaxGemmK)
     return PURO_ERR_SHAPE;
+  if (mode == PURO_WGRAD_TM && (M % 16 != 0 || N % 16 != 0 || M >= (int64_t(1) << 30) || N >= (int64_t(1) << 30)))
+    return PURO_ERR_SHAPE;   // 16-byte code rows; 4 rows of either operand index in 32 bits
   if (M == 0 || N == 0) return PURO_OK;
   if (!out) return PURO_ERR_NULL;
   const int64_t osz = out_dtype == PURO_OUT_F32 ? 4 : 2;
@@ -225,7 +244,7 @@ puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, co
     if (!aligned16(a) || !aligned16(sa) || !aligned16(b) || !aligned16(sb)) return PURO_ERR_ALIGN;
     if (plan.ws_bytes > 0 && !aligned16(workspace)) return PURO_ERR_ALIGN;
     const int64_t nk = cdiv(K, 128);
-    const int64_t sb_elems = mode == PURO_WGRAD ? nk * N : cdiv(N, 128) * nk;
+    const int64_t sb_elems = mode == PURO_WGRAD || mode == PURO_WGRAD_TM ? nk * N : cdiv(N, 128) * nk;
     const Range in[] = {rng(a, M * K), rng(sa, nk * M * 4), rng(b, N * K), rng(sb, sb_elems * 4)};
     const Range outs[] = {rng(out, M * N * osz), rng(workspace, (int64_t)plan.ws_bytes)};
     if (any_alias(in, 4, outs, 2)) return PURO_ERR_ALIAS;

@@ -209,6 +209,47 @@ __device__ __forceinline__ void dma_slice8ab(const void *abase, const void *bbas
       : "memory", "scc");
 }
 
+// The 8 copies of one token-major slice for this wave: copy j brings tile rows
+// 16w + 4j .. 16w + 4j + 3 of A (at `lds` + 1024 j) and of B (32 KB further),
+// 256 bytes each.  The row step is folded into the eight 64-bit bases; the
+// lane offsets repeat with the parity of j.
+__device__ __forceinline__ void dma_slice8kt(const void *a0, const void *a1, const void *a2, const void *a3,
+                                             const void *b0, const void *b1, const void *b2, const void *b3,
+                                             uint32_t va0, uint32_t va1, uint32_t vb0, uint32_t vb1, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %13\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, %1\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %11, %5\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %10, %2\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %12, %6\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %9, %3\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %11, %7\n\t"
+      "s_sub_u32 m0, m0, 0x7c00\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %10, %4\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %12, %8\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "s"(a0), "s"(a1), "s"(a2), "s"(a3), "s"(b0), "s"(b1), "s"(b2), "s"(b3), "v"(va0), "v"(va1), "v"(vb0),
+        "v"(vb1), "s"(lds)
+      : "memory", "scc");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -261,10 +302,11 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 // slices as one stream: the first slice of the next item is copied while the
 // last slice of the current one is computed, and the current item's output
 // leaves with direct global stores that drain while the next item computes.
-template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false>
+template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false, bool kKT = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(!kAcc || (!kBf16Out && !kToWs), "accumulate mode stores fp32 directly");
   static_assert(!kGlu || (!kRowScaledB && kBf16Out && !kToWs && !kAcc), "the SwiGLU epilogue follows an fprop");
+  static_assert(!kKT || (kRowScaledB && !kGlu), "token-major operands are the wgrad's");
   // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
   __shared__ __align__(1024) uint8_t smem[2][2][kSliceBytes];
   __shared__ __align__(16) float sscale[2][2][kBM];
@@ -295,10 +337,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // Interior tiles: lane offsets (row group j, row rig, logical chunk) are
   // shared by A and B; the wave's first row group and the K slice go into the
   // scalar bases.
-  const uint32_t voff0 = (uint32_t)(rig * K + dma_chunk(lane, 0));
-  const uint32_t voff1 = (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
-  const uint32_t voff2 = (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
-  const uint32_t voff3 = (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
+  // Token-major operands (kKT): tile row k holds 256 bytes (16 chunks of 16
+  // M or N values) of token k of the slice; chunk c of row k sits at chunk
+  // c ^ kt_swz(k), kt_swz(k) = (k & 7) | ((k >> 5) & 1) << 3, so that the
+  // transposing fragment reads below (rows 32q + 8s + r, r < 8) are free of
+  // bank conflicts.  Lane l of copy j fills row 16w + 4j + l/16 at physical
+  // chunk l % 16; the offsets depend on j only through its parity.
+  auto kt_voff = [&](int j, int64_t ld) -> uint32_t {
+    const int kr = 4 * j + (lane >> 4);                       // row within the wave's 16 (< 16)
+    const int sw = (kr & 7) | (((w >> 1) & 1) << 3);          // kt_swz(16w + kr)
+    return (uint32_t)((lane >> 4) * ld + (((lane & 15) ^ sw) << 4));
+  };
+  const uint32_t voff0 = kKT ? kt_voff(0, g.M) : (uint32_t)(rig * K + dma_chunk(lane, 0));
+  const uint32_t voff1 = kKT ? kt_voff(1, g.M) : (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
+  const uint32_t voff2 = kKT ? kt_voff(0, g.N) : (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
+  const uint32_t voff3 = kKT ? kt_voff(1, g.N) : (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
 
   // Per-lane values that only edge tiles, the ragged last slice and the scale
   // copies need are recomputed from an opaque lane id at each call, so that
@@ -346,7 +399,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const int i = r & 7;
     return (int64_t)(4 * (r >> 3)) + (i < 4 ? i : g.I + i - 4);
   };
+  auto issue_slice_kt = [&](const Tile &tl, int kb, int buf) {
+    const uint32_t la = lds0 + buf * 2 * kSliceBytes;
+    const int64_t k0 = (int64_t)kb * kBK + 16 * w;             // first token row of the wave's copies
+    if (tl.rows_a == kBM && tl.rows_b == kBN && !(ktail && kb == g.nk - 1)) {
+      const uint8_t *pa = g.a + k0 * g.M + tl.m0;
+      const uint8_t *pb = g.b + k0 * g.N + tl.n0;
+      dma_slice8kt(pa, pa + 4 * g.M, pa + 8 * g.M, pa + 12 * g.M, pb, pb + 4 * g.N, pb + 8 * g.N, pb + 12 * g.N,
+                   voff0, voff1, voff2, voff3, la + w * 4096);
+    } else {
+      // edge tiles and the ragged last slice: chunks past M / N and rows past K read a zero page
+      int ln = __lane_id();
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 4 * j + (ln >> 4);
+        const int64_t kg = k0 + kr;
+        const int c = (ln & 15) ^ ((kr & 7) | (((w >> 1) & 1) << 3));
+        const bool kin = kg < g.K;
+        const uint8_t *pa = kin && 16 * c < tl.rows_a ? g.a + kg * g.M + tl.m0 + 16 * c : g_zero16;
+        const uint8_t *pb = kin && 16 * c < tl.rows_b ? g.b + kg * g.N + tl.n0 + 16 * c : g_zero16;
+        dma16_v(pa, la + w * 4096 + j * 1024);
+        dma16_v(pb, la + kSliceBytes + w * 4096 + j * 1024);
+      }
+    }
+    issue_scales(tl, kb, buf);
+  };
   auto issue_slice = [&](const Tile &tl, int kb, int buf) {
+    if constexpr (kKT) {
+      issue_slice_kt(tl, kb, buf);
+      return;
+    }
     const int kofs = kb * kBK;
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const uint8_t *a_tile = g.a + (int64_t)tl.m0 * g.K;
@@ -420,14 +503,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // A fragment of m-block mb, B fragment of n-block nb (compile-time after unrolling)
+  // Token-major tiles: a transposing LDS read (ds_read_b64_tr_b8) lets a group
+  // of 16 lanes supply 16 rows of 8 bytes and gives lane i byte i % 8 of rows
+  // 2r + i / 8 (r < 8).  With row 2r + h = 8 bytes of token 8s + r at columns
+  // r0 + 8h .., lane (q, fr) receives tokens 32q + 8s .. +7 of column r0 + fr:
+  // four reads (s = 0..3) make the 32 bytes of K that the MFMA takes from it.
+  const uint32_t tr_lane = (uint32_t)((32 * q + (fr >> 1)) * 256 + 8 * (fr & 1));
+  const uint32_t tr_swz = (uint32_t)((fr >> 1) | ((q & 1) << 3));     // kt_swz of the lane's rows
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  auto frag_tr = [&](const uint8_t *tile, int r0) -> v8i {
+    const uint32_t a = lds_addr(tile) + tr_lane + ((((uint32_t)r0 >> 4) ^ tr_swz) << 4);
+    v8i out;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i *)(a + 2048u * s2));
+      out[2 * s2] = v.x;
+      out[2 * s2 + 1] = v.y;
+    }
+    return out;
+  };
   auto load_fragA = [&](const uint8_t *base, int mb) -> v8i {
+    if constexpr (kKT) return frag_tr(base, wm * 64 + mb * 16);
     return frag(base + (wm * 64 + mb * 16) * kBK, (mb & 1) ? aoff1 : aoff0);
   };
   auto load_fragB = [&](const uint8_t *base, int nb) -> v8i {
+    if constexpr (kKT) return frag_tr(base, wn * 128 + nb * 16);
     return frag(base + (wn * 128 + 32 * (nb >> 1) + 4 * (nb & 1)) * kBK, (nb & 1) ? boff1 : boff0);
   };
   // first B-fragment column of n-block nb seen by lane (q, fr), relative to the wave's 128
-  auto colB = [&](int nb) { return 32 * (nb >> 1) + 4 * (nb & 1) + 8 * q; };
+  // (token-major tiles: the 16 fragment rows are 16 consecutive columns)
+  auto colB = [&](int nb) { return kKT ? 16 * nb + 4 * q : 32 * (nb >> 1) + 4 * (nb & 1) + 8 * q; };
 
   // ---- K loop.  Slice s of the stream is computed from buffer s & 1 while
   // slice s+1 is copied into the other one.  The barrier that publishes slice
@@ -505,27 +610,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       // then VALU groups between the MFMAs
       constexpr int kV = kRowScaledB ? 8 : 4;
       constexpr int kS = kRowScaledB ? 1 : 0;
+      constexpr int kF = 2;  // LDS reads per group (also for the 4-read token-major fragments: it schedules better)
       if (nb == 0) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);                // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x100, kF + kS, 0);               // LDS reads
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
           if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, kGlu ? 2 : 1, 0);  // VALU
         }
       } else if (nb < 7) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + kS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kF + kS, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
       } else {
-        if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (kPre) __builtin_amdgcn_sched_group_barrier(0x100, kF, 0);
         }
       }
     }
@@ -663,8 +769,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       return __builtin_bit_cast(uint32_t, __builtin_convertvector(h ? __builtin_shufflevector(v, v, 2, 3)
                                                                     : __builtin_shufflevector(v, v, 0, 1), v2bf));
     };
+    if constexpr (kKT) {
+      // token-major tiles: lane (q, fr) holds columns 16nb + 4q .. +3 of n-block nb
+      if (tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0) {
+        const int64_t lk = (int64_t)fr * g.N + 4 * q;
+        if constexpr (kBf16Out && !kToWs) {
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N + lk;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+              *reinterpret_cast<u32x2 *>(ob + 16 * nb) = (u32x2){pk(acc[mb][nb], 0), pk(acc[mb][nb], 1)};
+          }
+        } else {
+          float *o = (kToWs ? g.ws + (int64_t)tl.split * g.M * g.N : reinterpret_cast<float *>(g.out)) + wbase;
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) {
+            float *ob = o + (int64_t)(mb * 16) * g.N + lk;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+              v4f *p0 = reinterpret_cast<v4f *>(ob + 16 * nb);
+              if constexpr (kAcc) {
+                const v4f o0 = *p0;
+                *p0 = o0 + acc[mb][nb];
+              } else {
+                *p0 = acc[mb][nb];
+              }
+            }
+          }
+        }
+        return;
+      }
+    }
     if constexpr (kBf16Out && !kToWs) {
-      const bool fast = tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 7) == 0;
+      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 7) == 0;
       if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -696,7 +834,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     } else {
       float *o = (kToWs ? g.ws + (int64_t)tl.split * g.M * g.N : reinterpret_cast<float *>(g.out)) + wbase;
-      const bool fast = tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0;
+      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0;
       if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -869,6 +1007,19 @@ static int compute_units() {
   return cached[dev];
 }
 
+// One kernel of the family for a mode (RB: row-scaled B; KT: token-major operands).
+template <bool RB, bool KT>
+static void launch_mode(const dim3 &grid, hipStream_t stream, const GemmArgs &g, bool to_ws, bool acc, bool bf16) {
+  if (to_ws)
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, true, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+  else if (acc)
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, true, false, KT>), grid, dim3(kThreads), 0, stream, g);
+  else if (bf16)
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, true, false, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+}
+
 hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                     void *out, bool bf16_out, bool accumulate, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream) {
@@ -888,23 +1039,11 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
   g.splits = p.splits; g.spl = p.spl;
   const dim3 grid((unsigned)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n * p.splits, compute_units()));
-  const bool row_b = mode == 2;
+  const bool row_b = mode == 2 || mode == 3;
   const bool to_ws = p.splits > 1;
-#define PURO_LAUNCH(RB, BF, WS) \
-  hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, BF, WS>), grid, dim3(kThreads), 0, stream, g)
-#define PURO_LAUNCH_ACC(RB) \
-  hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, true>), grid, dim3(kThreads), 0, stream, g)
-  if (to_ws) {
-    if (row_b) PURO_LAUNCH(true, false, true); else PURO_LAUNCH(false, false, true);
-  } else if (accumulate) {
-    if (row_b) PURO_LAUNCH_ACC(true); else PURO_LAUNCH_ACC(false);
-  } else if (bf16_out) {
-    if (row_b) PURO_LAUNCH(true, true, false); else PURO_LAUNCH(false, true, false);
-  } else {
-    if (row_b) PURO_LAUNCH(true, false, false); else PURO_LAUNCH(false, false, false);
-  }
-#undef PURO_LAUNCH
-#undef PURO_LAUNCH_ACC
+  if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
+  else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
+  else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !to_ws) return err;
   const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 8192);

@@ -14,6 +14,10 @@ hipError_t run_quant_w_128x128(const uint16_t *w, int64_t R, int64_t C, uint8_t 
                                hipStream_t stream);
 hipError_t run_quant_t_act(const uint16_t *x, int64_t R, int64_t C, uint8_t *qt, float *st,
                            uint8_t *q, float *s, hipStream_t stream);
+// 128x1 codes of x in x's own layout (qc [R][C], sc [ceil(R/128)][C]); q, s
+// optional 1x128 codes from the same read.
+hipError_t run_quant_act_128x1(const uint16_t *x, int64_t R, int64_t C, uint8_t *qc, float *sc, uint8_t *q,
+                               float *s, hipStream_t stream);
 hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, float *st,
                          uint8_t *q, float *s, hipStream_t stream);
 hipError_t run_swiglu_quant(const uint16_t *gu, int64_t R, int64_t I, uint8_t *q, float *s, uint8_t *qt,

@@ -70,14 +70,17 @@ __device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *
 // kBlock:  one 128x128 scale                         -> row-major and/or transposed output
 // kSwiGLU: the block's values are h = SwiGLU(gate, up) of a [R][2C] gate/up
 //          input (gate = first C columns), computed in registers
-template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false>
+// kTRow: the 128x1 codes (kCol) leave in the input's own [R][C] layout
+// instead of transposed, for a wgrad that reads its operands token-major.
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false, bool kTRow = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
+  static_assert(!kTRow || (kCol && kWriteT), "the untransposed form is that of the 128x1 codes");
   __shared__ float lds_part[16 * kTile];                 // column partial maxima [rg][c]
   __shared__ float lds_rowamax[kTile];
   __shared__ __align__(16) float lds_rows[kTile], lds_rowr[kTile];
   __shared__ __align__(16) float lds_cols[kTile], lds_colr[kTile];
   __shared__ float lds_wmax[4];
-  __shared__ __align__(16) uint8_t lds_t[kWriteT ? kTile * kTile : 16];
+  __shared__ __align__(16) uint8_t lds_t[kWriteT && !kTRow ? kTile * kTile : 16];
 
   const int t = threadIdx.x;
   const int cc = t & 15, rg = t >> 4;
@@ -299,6 +302,27 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) fast &= cs[c] >= kFastDivMinScale;
     refresh();
+    if constexpr (kTRow) {
+      // row k of the thread's 8x8 block with its 8 column scales: one 8-byte
+      // store per row, like the row-wise codes
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float v[8];
+        if (fast) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = quot_fast(el(k, c), cs[c], cr[c]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = cs[c] >= kFastDivMinScale ? quot_fast(el(k, c), cs[c], cr[c]) : el(k, c) / cs[c];
+        }
+        u32x2 o;
+        o.x = pack4_e4m3(v[0], v[1], v[2], v[3]);
+        o.y = pack4_e4m3(v[4], v[5], v[6], v[7]);
+        const int64_t r = r0 + k;
+        if (cvalid && r < a.R) __builtin_nontemporal_store(o, reinterpret_cast<u32x2 *>(a.qt + r * a.C + c0));
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       float v[8];
@@ -476,11 +500,11 @@ __global__ __launch_bounds__(256) void requant_t_kernel(RequantArgs a) {
   flush_transposed(lds_t, a.qt, a.R, a.C, bi, bj, t);
 }
 
-template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false>
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false, bool kTRow = false>
 static hipError_t launch_quant(const QuantArgs &a, hipStream_t stream) {
   const int64_t blocks = a.ni * a.nj;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((quant_block_kernel<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU>),
+  hipLaunchKernelGGL((quant_block_kernel<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU, kTRow>),
                      dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -521,6 +545,17 @@ hipError_t run_quant_t_act(const uint16_t *x, int64_t R, int64_t C, uint8_t *qt,
   a.s = s;
   if (q) return launch_quant<true, true, false, true, true>(a, stream);
   return launch_quant<false, true, false, false, true>(a, stream);
+}
+
+hipError_t run_quant_act_128x1(const uint16_t *x, int64_t R, int64_t C, uint8_t *qc, float *sc, uint8_t *q,
+                               float *s, hipStream_t stream) {
+  QuantArgs a = make_args(x, R, C);
+  a.qt = qc;          // [R][C]: the 128x1 codes in x's layout
+  a.st = sc;
+  a.q = q;
+  a.s = s;
+  if (q) return launch_quant<true, true, false, true, true, false, true>(a, stream);
+  return launch_quant<false, true, false, false, true, false, true>(a, stream);
 }
 
 hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, float *st,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 5
+#define PURO_ABI_VERSION 6
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -74,7 +74,9 @@ typedef enum {
 typedef enum {
     PURO_FPROP = 0,   /* Y  = X  W^T : a = act codes of X  [T][K_in],      b = weight codes of W [N_out][K_in] */
     PURO_DGRAD = 1,   /* dX = dY W   : a = act codes of dY [T][N_out],     b = transposed weight codes [K_in][N_out] */
-    PURO_WGRAD = 2    /* dW = dY^T X : a = 128x1 codes of dY [N_out][T],   b = 128x1 codes of X [K_in][T] */
+    PURO_WGRAD = 2,   /* dW = dY^T X : a = 128x1 codes of dY [N_out][T],   b = 128x1 codes of X [K_in][T] */
+    PURO_WGRAD_TM = 3 /* dW = dY^T X from token-major codes: a = 128x1 codes of dY [T][N_out],
+                         b = 128x1 codes of X [T][K_in], as puro_quant_act_128x1 writes them */
 } puro_gemm_mode;
 
 typedef enum { PURO_OUT_F32 = 0, PURO_OUT_BF16 = 1 } puro_out_dtype;
@@ -119,6 +121,23 @@ puro_status puro_quant_w_128x128(const uint16_t *w, int64_t rows, int64_t cols,
  */
 puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *qt, float *st, uint8_t *q_row, float *s_row,
+                                 puro_stream_t stream);
+
+/*
+ * puro_quant_act_128x1 -- the 128x1 tiles of puro_quant_transpose(PURO_T_ACT)
+ * (128 consecutive rows of one column share a scale), with the codes left in
+ * x's own layout instead of transposed: the wgrad operand in the token-major
+ * form that puro_gemm_fp8_blockwise(PURO_WGRAD_TM) reads.  Writing the codes
+ * untransposed keeps every store a row segment.
+ *   qc [rows][cols] uint8: qc[r][c] = the 128x1 code of x[r][c]
+ *      (= qt[c][r] of puro_quant_transpose(PURO_T_ACT))
+ *   sc [ceil(rows/128)][cols] fp32: sc[i][c] is the scale of x[128i..][c]
+ *   q_row, s_row (optional, both NULL or both set): the same pass also writes
+ *      exactly what puro_quant_act_1x128(x) writes.
+ * cols must be a multiple of 16; rows is free.
+ */
+puro_status puro_quant_act_128x1(const uint16_t *x, int64_t rows, int64_t cols,
+                                 uint8_t *qc, float *sc, uint8_t *q_row, float *s_row,
                                  puro_stream_t stream);
 
 /*
@@ -186,6 +205,10 @@ size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int6
  *   sb   FPROP/DGRAD: [ceil(N/128)][ceil(K/128)] fp32, sb(n, k) = sb[n/128][k/128]
  *        WGRAD:       [ceil(K/128)][N] fp32,            sb(n, k) = sb[k/128][n]
  *   out  [M][N] fp32 or bf16 (round to nearest even)
+ * PURO_WGRAD_TM takes the operands token-major instead: a [K][M] and b [K][N]
+ * with a[k][m] and b[k][n] in place of a[m][k] and b[n][k] above, scales as
+ * for PURO_WGRAD; M and N must then be multiples of 16.  It gives exactly the
+ * bits PURO_WGRAD gives for the transposed operands.
  *   workspace / workspace_bytes: at least puro_gemm_workspace_bytes(mode, M, N, K)
  *        bytes of device memory (may be NULL when that is 0); its contents on
  *        entry do not matter.

@@ -32,7 +32,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FPROP, DGRAD, WGRAD = 0, 1, 2
+FPROP, DGRAD, WGRAD, WGRAD_TM = 0, 1, 2, 3
 TILE = 128
 
 _lib = None
@@ -188,6 +188,13 @@ def quant_act_128x1_t(x: np.ndarray):
     return qt, st
 
 
+def quant_act_128x1(x: np.ndarray):
+    """The 128x1 tiles of quant_act_128x1_t with the codes in x's own layout:
+    x uint16 [R][C] -> (q uint8 [R][C], s float32 [ceil(R/128)][C]), q[r][c] = qt[c][r]."""
+    qt, st = quant_act_128x1_t(x)
+    return np.ascontiguousarray(qt.T), st
+
+
 def quant_w_128x128_t(w: np.ndarray):
     """w: uint16 [R][C] -> (qt uint8 [C][R], st float32 [ceil(C/128)][ceil(R/128)])."""
     w = _u16(w)
@@ -261,6 +268,16 @@ def gemm_swiglu_quant(a, sa, b, sb, rows=None):
     return gu, h, q, s
 
 
+def _token_major(mode, a, b):
+    """WGRAD_TM takes the wgrad operands token-major ([K][M], [K][N]); the sum is
+    the wgrad's over the transposed arrays (a layout change only)."""
+    if mode != WGRAD_TM:
+        return mode, a, b
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.uint8).T)
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8).T)
+    return WGRAD, a, b
+
+
 def _gemm_args(mode, a, sa, b, sb):
     a = np.ascontiguousarray(a, dtype=np.uint8)
     b = np.ascontiguousarray(b, dtype=np.uint8)
@@ -281,6 +298,7 @@ def _gemm_args(mode, a, sa, b, sb):
 
 def gemm(mode: int, a, sa, b, sb) -> np.ndarray:
     """fp64 reference out[M][N] = sum_k deq(a)[m][k] * deq(b)[n][k]."""
+    mode, a, b = _token_major(mode, a, b)
     a, sa, b, sb, M, N, K = _gemm_args(mode, a, sa, b, sb)
     out = np.empty((M, N), dtype=np.float64)
     _load().orc_gemm(mode, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), M, N, K, _ptr(out))
@@ -299,6 +317,7 @@ def gemm_accumulate(mode: int, a, sa, b, sb, c) -> np.ndarray:
 
 def gemm_at(mode: int, a, sa, b, sb, ms, ns) -> np.ndarray:
     """fp64 reference values at positions (ms[i], ns[i])."""
+    mode, a, b = _token_major(mode, a, b)
     a, sa, b, sb, M, N, K = _gemm_args(mode, a, sa, b, sb)
     ms = np.ascontiguousarray(ms, dtype=np.int64)
     ns = np.ascontiguousarray(ns, dtype=np.int64)
@@ -314,6 +333,7 @@ def gemm_at(mode: int, a, sa, b, sb, ms, ns) -> np.ndarray:
 
 def deq_row_norms(mode: int, a, sa, b, sb):
     """(||A_m||_2 for each m, ||B_n||_2 for each n) of the dequantized operands, fp64."""
+    mode, a, b = _token_major(mode, a, b)
     a, sa, b, sb, M, N, K = _gemm_args(mode, a, sa, b, sb)
     na = np.empty(M, dtype=np.float64)
     nb = np.empty(N, dtype=np.float64)

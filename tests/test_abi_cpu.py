@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
+    assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose", "puro_quant_act_128x1",
                             "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
                             "puro_gemm_fp8_blockwise_accumulate", "puro_gemm_fp8_swiglu_quant",
                             "puro_status_str", "puro_abi_version"])
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 5
+    assert puro.puro_abi_version() == 6
     for s in range(10):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -91,6 +91,24 @@ def test_quant_transpose_validation():
     assert f(0, A0, 128, 128, A1, A2, A3 + 8, A4) == ALIGN
     assert f(0, A0, 128, 128, A1, A2, A1 + 1024, A4) == ALIAS  # q_row overlaps qt
     assert f(0, A0, 0, 128, None, None, None, None) == OK
+
+
+def test_quant_act_128x1_validation():
+    f = puro.puro_quant_act_128x1
+    assert f(A0, 128, 100, A1, A2, None, None) == SHAPE                   # cols not a multiple of 16
+    assert f(A0, -1, 128, A1, A2, None, None) == SHAPE
+    assert f(A0, 120, 128, A1, A2, None, None) != SHAPE                   # rows free
+    assert f(None, 0, 128, None, None, None, None) == OK
+    assert f(A0, 128, 128, A1, A2, A3, None) == NULL                      # q_row without s_row
+    assert f(A0, 128, 128, None, A2, None, None) == NULL
+    assert f(A0, 128, 128, A1, None, None, None) == NULL
+    assert f(A0 + 8, 128, 128, A1, A2, None, None) == ALIGN
+    assert f(A0, 128, 128, A1, A2 + 4, None, None) == ALIGN
+    assert f(A0, 128, 128, A1, A2, A3 + 2, A4) == ALIGN
+    assert f(A0, 128, 128, A0 + 4096, A2, None, None) == ALIAS            # codes inside x
+    assert f(A0, 128, 128, A1, A2, A1 + 64, A4) == ALIAS                  # row codes overlap the 128x1 codes
+    if no_gpu():
+        assert f(A0, 128, 128, A1, A2, A3, A4) == DEVICE
 
 
 def test_requant_validation():
@@ -147,9 +165,12 @@ def test_gemm_validation():
         a = dict(args, **kw)
         return f(mode, a["a"], a["sa"], a["b"], a["sb"], a["out"], od, M, N, K, ws, wsb)
 
-    assert call(mode=3) == MODE
+    assert call(mode=4) == MODE
     assert call(mode=-1) == MODE
     assert call(od=2) == DTYPE
+    assert call(mode=3, M=200) == SHAPE                   # token-major wgrad: M and N multiples of 16
+    assert call(mode=3, N=8) == SHAPE
+    assert call(mode=3, M=1 << 30, N=16, K=16) == SHAPE   # 4 rows of a must index in 32 bits
     assert call(K=100) == SHAPE
     assert call(M=-5) == SHAPE
     assert call(K=1 << 24) == SHAPE
@@ -175,7 +196,7 @@ def test_gemm_accumulate_validation():
         a = dict(args, **kw)
         return f(mode, a["a"], a["sa"], a["b"], a["sb"], a["out"], M, N, K, ws, wsb)
 
-    assert call(mode=3) == MODE
+    assert call(mode=4) == MODE
     assert call(K=100) == SHAPE
     assert call(M=0) == OK
     assert call(out=None) == NULL

@@ -1,8 +1,8 @@
 """The C calls enqueue kernels only (no allocation, no memset, no host wait), so
 a caller can capture them in a HIP graph.  One linear's forward and backward
 operands, its three GEMMs (a split-K wgrad among them), the accumulating
-wgrad, the requantizer, the fused SwiGLU and the gate/up fprop with the SwiGLU
-epilogue are captured once and replayed
+wgrad, the requantizer, the fused SwiGLU, the gate/up fprop with the SwiGLU
+epilogue and the token-major wgrad path are captured once and replayed
 several times, with eager work between the replays; every replay must give
 the eager results bit for bit."""
 import numpy as np
@@ -44,6 +44,9 @@ class Buffers:
         self.dw_acc = e((N, K), f32)
         self.gu2 = e((T, N), torch.bfloat16)                  # W read as a gate/up weight of inter N / 2
         self.fq, self.fs = e((T, N // 2)), e((N // 256, T), f32)
+        self.xc, self.xcs = e((T, K)), e((cdiv(T, 128), K), f32)        # token-major 128x1 codes of X and dY
+        self.dc, self.dcs = e((T, N)), e((cdiv(T, 128), N), f32)
+        self.dw_tm = e((N, K), f32)
         need = max(puro.puro_gemm_workspace_bytes(m, *s) for m, s in
                    ((puro.FPROP, (T, N, K)), (puro.DGRAD, (T, K, N)), (puro.WGRAD, (N, K, T))))
         self.work = e((max(need, 16),))
@@ -52,7 +55,7 @@ class Buffers:
     def outputs(self):
         return [self.xq, self.xs, self.xqt, self.xst, self.wq, self.ws_, self.wqt, self.wst, self.dq, self.ds,
                 self.dqt, self.dst, self.rqt, self.rst, self.hq, self.hs, self.hqt, self.hst, self.y, self.dx,
-                self.dw, self.dw_acc, self.gu2, self.fq, self.fs]
+                self.dw, self.dw_acc, self.gu2, self.fq, self.fs, self.xc, self.xcs, self.dc, self.dcs, self.dw_tm]
 
     def enqueue(self):
         st = torch.cuda.current_stream().cuda_stream
@@ -74,6 +77,10 @@ class Buffers:
                                                    p(self.dw_acc), N, K, T, p(self.work), self.need, st))
         ok(puro.puro_gemm_fp8_swiglu_quant(p(self.xq), p(self.xs), p(self.wq), p(self.ws_), T, N // 2, K,
                                            p(self.gu2), p(self.fq), p(self.fs), st))
+        ok(puro.puro_quant_act_128x1(p(self.x), T, K, p(self.xc), p(self.xcs), None, None, st))
+        ok(puro.puro_quant_act_128x1(p(self.dy), T, N, p(self.dc), p(self.dcs), None, None, st))
+        ok(puro.puro_gemm_fp8_blockwise(puro.WGRAD_TM, p(self.dc), p(self.dcs), p(self.xc), p(self.xcs), p(self.dw_tm),
+                                        puro.OUT_F32, N, K, T, p(self.work), self.need, st))
 
 
 def snapshot(buf):
