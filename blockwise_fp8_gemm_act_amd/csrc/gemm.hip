@@ -50,7 +50,12 @@
 //    h = bf16(silu(g) * u) -- the down projection's FP8 input -- with the
 //    bf16 gate/up output optional.  The epilogue runs after the item's last
 //    slice and does not overlap MFMA work, which makes it cost more than the
-//    separate SwiGLU quantizer pass unless the gate/up output is dropped.
+//    separate SwiGLU quantizer pass unless the gate/up output is dropped;
+//  - token-major wgrad (kKT): A and B arrive as [K][M] / [K][N] codes (the
+//    128x1 codes left untransposed by their quantizer); slices are copied as
+//    token rows and the MFMA fragments are assembled by transposing LDS
+//    reads (ds_read_b64_tr_b8), four per fragment.  Products and their order
+//    are those of the wgrad on the transposed operands.
 #include "device_common.h"
 #include "launch.h"
 
@@ -307,7 +312,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(!kAcc || (!kBf16Out && !kToWs), "accumulate mode stores fp32 directly");
   static_assert(!kGlu || (!kRowScaledB && kBf16Out && !kToWs && !kAcc), "the SwiGLU epilogue follows an fprop");
   static_assert(!kKT || (kRowScaledB && !kGlu), "token-major operands are the wgrad's");
-  // [buf][A/B][256 rows x 128 B] operand slices; [buf][sA/sB][256] scales
+  // [buf][A/B][256 rows x 128 B] operand slices (token-major: 128 token rows
+  // x 256 B); [buf][sA/sB][256] scales
   __shared__ __align__(1024) uint8_t smem[2][2][kSliceBytes];
   __shared__ __align__(16) float sscale[2][2][kBM];
   __shared__ __align__(16) uint32_t xamax[kGlu ? 2 * kBM : 1];   // SwiGLU: row maxima of |h| per half tile
