@@ -18,7 +18,9 @@
 // reciprocals are computed once per tile by one thread and shared through
 // LDS.  Transposed codes are assembled in LDS (8-byte slots XOR-swizzled by
 // the column group, so both the 8-byte writes and the 16-byte reads are free
-// of bank conflicts) and leave as 128-byte row segments.
+// of bank conflicts) and leave as 128-byte row segments.  The token-major form
+// of the 128x1 codes skips the transpose: they leave in the input's layout,
+// 8 bytes per row of the thread's block, like the row-wise codes.
 #include "device_common.h"
 #include "launch.h"
 
