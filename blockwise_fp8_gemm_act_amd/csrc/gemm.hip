@@ -59,6 +59,7 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace puro {
@@ -1000,17 +1001,18 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
 }
 
 // Compute units of the current device (one persistent workgroup each),
-// queried once per device.
+// queried once per device; callers on several host threads may race to fill
+// an entry, which is harmless since they all store the same count.
 static int compute_units() {
-  static int cached[64];
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // One kernel of the family for a mode (RB: row-scaled B; KT: token-major operands).
