@@ -86,6 +86,8 @@ struct GemmArgs {
   int tiles_m, tiles_n;
   int splits;      // K-loop splits (1: no workspace)
   int spl;         // slices per split
+  int tile0;       // this launch covers output tiles tile0 .. tile0 + ntiles - 1
+  int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -272,10 +274,9 @@ struct Tile {
 
 // glu: the tile covers h columns n0 .. n0+127 (B rows: 128 gate + 128 up rows).
 __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = false) {
-  const int total_tiles = g.tiles_m * g.tiles_n;
   Tile t;
-  t.split = item / total_tiles;
-  const int tile = item - t.split * total_tiles;
+  t.split = item / g.ntiles;
+  const int tile = g.tile0 + (item - t.split * g.ntiles);
   const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
   const int tn = tile / g.tiles_m;
   t.m0 = tm * kBM;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const int lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int total_items = g.tiles_m * g.tiles_n * g.splits;
+  const int total_items = g.ntiles * g.splits;
   int item = blockIdx.x;
   if (item >= total_items) return;
   const int K = (int)g.K;
@@ -947,6 +948,33 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, voi
   }
 }
 
+// The same over the output tiles tile0 .. tile0 + ntiles - 1 only (the other
+// tiles were computed whole and stored directly): element e of the range is
+// row (e / 256) % 256, column e % 256 of tile tile0 + e / 65536.
+template <bool kBf16Out, bool kAcc = false>
+__global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *ws, void *out, int64_t M, int64_t N,
+                                                                  int tiles_m, int tile0, int ntiles, int splits) {
+  static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
+  const int64_t MN = M * N;
+  const int64_t total = (int64_t)ntiles * kBM * kBN;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const int tile = tile0 + (int)(e / (kBM * kBN));
+    const int r = (int)(e / kBN) % kBM, c = (int)(e % kBN);
+    const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * kBN + c;
+    if (m >= M || n >= N) continue;
+    const int64_t i = m * N + n;
+    float v = ws[i];
+    for (int s = 1; s < splits; ++s) v += ws[(int64_t)s * MN + i];
+    if constexpr (kBf16Out)
+      reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16_rne(v);
+    else if constexpr (kAcc)
+      reinterpret_cast<float *>(out)[i] += v;
+    else
+      reinterpret_cast<float *>(out)[i] = v;
+  }
+}
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void fill_zero_kernel(void *out, int64_t MN) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -971,30 +999,49 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
   p.tiles_m = (int)((M + kBM - 1) / kBM);
   p.tiles_n = (int)((N + kBN - 1) / kBN);
   p.splits = 1;
+  p.whole = 0;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   // Split the K loop when the output tiles fill the 256 compute units poorly
   // (a last round of tiles that leaves units idle, or fewer tiles than units).
-  // Estimated time with s splits: rounds of 256 work items, each of ceil(nk/s)
-  // slices plus about 2 slices of fixed cost (first copy, epilogue) at about
-  // 1.9 us per slice, plus the workspace traffic (every split writes an fp32
-  // partial of the output and the reduction reads it back) at about 4 TB/s.
-  // More splits must win by 3%; at least 4 slices per split.
+  // Estimated time of rounds of 256 work items, each of its slices plus about
+  // 2 slices of fixed cost (first copy, epilogue) at about 1.9 us per slice,
+  // plus the workspace traffic (every split writes an fp32 partial of its
+  // tiles and the reduction reads it back) at about 4 TB/s.  Two forms:
+  //  - every tile split s ways;
+  //  - when the tiles fill w >= 1 whole rounds and leave r more, the first
+  //    256w tiles computed whole by a first launch (direct stores, no
+  //    workspace) and only the last r split s ways by a second one (about
+  //    3 us more for the extra launch).
+  // Splitting must win by 3%; at least 4 slices per split.
   if (tiles > 0 && p.nk > 0) {
+    const double us = 1.9e-6, bw = 4.0e12, tile_bytes = 4.0 * kBM * kBN;
     double best = 0.0;
     for (int s = 1; s <= 8; ++s) {
       const int spl = (p.nk + s - 1) / s;
       if (s > 1 && (spl < 4 || (p.nk + spl - 1) / spl != s)) continue;
-      const double rounds = (double)((tiles * s + 255) / 256);
-      const double t = rounds * (spl + 2) * 1.9e-6 +
-                       (s > 1 ? 2.0 * s * (double)M * (double)N * 4.0 / 4.0e12 : 0.0);
+      const double t = (double)((tiles * s + 255) / 256) * (spl + 2) * us +
+                       (s > 1 ? 2.0 * s * (double)M * (double)N * 4.0 / bw : 0.0);
       if (s == 1 || t < best * 0.97) {
         best = t;
         p.splits = s;
       }
     }
+    const int64_t w = tiles / 256, r = tiles % 256;
+    for (int s = 2; w > 0 && r > 0 && s <= 8; ++s) {
+      const int spl = (p.nk + s - 1) / s;
+      if (spl < 4 || (p.nk + spl - 1) / spl != s) continue;
+      const double t = (double)w * (p.nk + 2) * us + (double)((r * s + 255) / 256) * (spl + 2) * us +
+                       2.0 * s * (double)r * tile_bytes / bw + 3.0e-6;
+      if (t < best * 0.97) {
+        best = t;
+        p.splits = s;
+        p.whole = (int)(w * 256);
+      }
+    }
   }
   p.spl = (p.nk + p.splits - 1) / p.splits;
   if (p.spl > 0) p.splits = (p.nk + p.spl - 1) / p.spl;
+  if (p.splits == 1) p.whole = 0;
   p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
   (void)mode;
   return p;
@@ -1045,15 +1092,38 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.out = out; g.ws = (float *)ws;
   g.M = M; g.N = N; g.K = K;
   g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
-  g.splits = p.splits; g.spl = p.spl;
-  const dim3 grid((unsigned)std::min<int64_t>((int64_t)p.tiles_m * p.tiles_n * p.splits, compute_units()));
+  const int tiles = p.tiles_m * p.tiles_n;
   const bool row_b = mode == 2 || mode == 3;
+  // one persistent launch over tiles [tile0, tile0 + ntiles), each split s ways
+  auto launch = [&](int tile0, int ntiles, int s, int spl, bool to_ws) {
+    g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
+    const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
+    if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
+    return hipGetLastError();
+  };
+  hipError_t err = hipSuccess;
+  if (p.whole > 0 && (err = launch(0, p.whole, 1, p.nk, false)) != hipSuccess) return err;
   const bool to_ws = p.splits > 1;
-  if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
-  else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
-  else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
-  hipError_t err = hipGetLastError();
+  err = launch(p.whole, tiles - p.whole, p.splits, p.spl, to_ws);
   if (err != hipSuccess || !to_ws) return err;
+  if (p.whole > 0) {
+    const int64_t n = (int64_t)(tiles - p.whole) * kBM * kBN;
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+    const float *w = (const float *)ws;
+    const int nt = tiles - p.whole;
+    if (bf16_out)
+      hipLaunchKernelGGL(splitk_reduce_tiles_kernel<true>, dim3(blocks), dim3(256), 0, stream, w, out, M, N, p.tiles_m,
+                         p.whole, nt, p.splits);
+    else if (accumulate)
+      hipLaunchKernelGGL((splitk_reduce_tiles_kernel<false, true>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
+                         p.tiles_m, p.whole, nt, p.splits);
+    else
+      hipLaunchKernelGGL(splitk_reduce_tiles_kernel<false>, dim3(blocks), dim3(256), 0, stream, w, out, M, N, p.tiles_m,
+                         p.whole, nt, p.splits);
+    return hipGetLastError();
+  }
   const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 8192);
   if (bf16_out)
     hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
@@ -1090,6 +1160,7 @@ hipError_t run_gemm_swiglu_quant(const uint8_t *a, const float *sa, const uint8_
   g.tiles_m = (int)((M + kBM - 1) / kBM);
   g.tiles_n = (int)(I / kBK);
   g.splits = 1; g.spl = g.nk;
+  g.tile0 = 0; g.ntiles = g.tiles_m * g.tiles_n;
   g.I = I; g.hq = hq; g.hs = hs;
   const dim3 grid((unsigned)std::min<int64_t>((int64_t)g.tiles_m * g.tiles_n, compute_units()));
   hipLaunchKernelGGL((gemm_fp8_bw_kernel<false, true, false, false, true>), grid, dim3(kThreads), 0, stream, g);

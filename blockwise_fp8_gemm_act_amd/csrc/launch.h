@@ -30,6 +30,7 @@ struct GemmPlan {
   int tiles_m, tiles_n;
   int splits;      // K-loop splits
   int spl;         // slices per split
+  int whole;       // > 0: tiles 0 .. whole-1 run unsplit in a first launch, only the rest split
   size_t ws_bytes; // fp32 split-K partials
 };
 

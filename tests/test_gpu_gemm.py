@@ -110,6 +110,47 @@ def test_repeated_calls_bitwise_identical(orc, mode, M, N, K):
         assert torch.equal(r1.view(iv), r2.view(iv)), "mode %d %dx%dx%d %s" % (mode, M, N, K, dtype)
 
 
+def whole_then_split_check(orc, mode, a, sa, b, sb, out, dtype, what):
+    """Every output of the split tiles (rows 1024.., columns 10752..) and samples of the rest."""
+    M, N = a.shape[0], b.shape[0]
+    rm, rn = np.meshgrid(np.arange(1024, M), np.arange(10752, N), indexing="ij")
+    sm, sn = sample_positions(M, N, 4096, M + N)
+    ms, ns = np.concatenate([rm.ravel(), sm]), np.concatenate([rn.ravel(), sn])
+    ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
+    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
+    check_gemm_values(out_np(out)[ms, ns], ref, na[ms], nb[ns], dtype == torch.bfloat16, orc, what)
+
+
+@pytest.mark.parametrize("mode", [FPROP, WGRAD])
+def test_whole_tiles_then_split_remainder(orc, mode):
+    """258 output tiles (6 x 43) at 8 K slices: tiles 0-255 fill the compute units once and run whole in a
+    first launch; only the last two, ragged in rows, columns and K, are split over K by a second launch and
+    summed by the tile-range reduction.  fp32 and bf16 out; two calls give the same bits."""
+    M, N, K = 1480, 10900, 1008
+    assert puro.puro_gemm_workspace_bytes(mode, M, N, K) > 0
+    a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=258)
+    for dtype in (torch.float32, torch.bfloat16):
+        r1 = run_gpu(mode, a, sa, b, sb, dtype)
+        whole_then_split_check(orc, mode, a, sa, b, sb, r1, dtype, "mode %d %s" % (mode, dtype))
+        r2 = run_gpu(mode, a, sa, b, sb, dtype)
+        iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(r1.view(iv), r2.view(iv))
+
+
+def test_whole_tiles_then_split_remainder_accumulate(orc):
+    """The same plan in accumulate mode: whole tiles add in the GEMM's epilogue, split tiles in the
+    reduction; both are one fp32 addition of the plain result."""
+    M, N, K = 1480, 10900, 1008
+    a, sa, b, sb = quantized_operands(orc, WGRAD, M, N, K, seed=259)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    plain = to_np(run_gpu(WGRAD, a, sa, b, sb, torch.float32))
+    c = (np.random.default_rng(7).standard_normal((M, N)) * float(np.abs(plain).mean())).astype(np.float32)
+    out = dv(c)
+    puro.gemm_fp8_blockwise_accumulate(WGRAD, dv(a), dv(sa), dv(b), dv(sb), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), c + plain)
+
+
 def test_zero_k_writes_zeros():
     for dtype in (torch.float32, torch.bfloat16):
         a = torch.zeros((5, 0), dtype=torch.uint8, device="cuda")
@@ -129,11 +170,18 @@ def sample_positions(M, N, n, seed):
     return ms, ns
 
 
-@pytest.mark.parametrize("which", ["qkv_fprop", "mlp_down_dgrad", "mlp_down_wgrad"])
+@pytest.mark.parametrize("which", ["qkv_fprop", "mlp_down_dgrad", "mlp_down_wgrad", "gate_up_wgrad"])
 def test_workload_sizes_sampled(orc, which):
     """Full-size GEMMs, in the launch configuration the benchmark uses,
-    checked on 4096 sampled outputs plus the first and last rows."""
-    if which == "qkv_fprop":
+    checked on 4096 sampled outputs plus the first and last rows.  The gate/up
+    wgrad of the layer at 16384 tokens (384 tiles) runs its first 256 tiles
+    whole and splits the other 128 over K."""
+    if which == "gate_up_wgrad":
+        t = make("layer", names={"x_gate_up", "dy_gate_up"})
+        a, sa = orc.quant_act_128x1_t(bits(t["dy_gate_up"]))
+        b, sb = orc.quant_act_128x1_t(bits(t["x_gate_up"]))
+        mode, dtype = WGRAD, torch.float32
+    elif which == "qkv_fprop":
         t = make("qkv_fprop")
         a, sa = orc.quant_act_1x128(bits(t["x"]))
         b, sb = orc.quant_w_128x128(bits(t["w"]))
@@ -150,7 +198,8 @@ def test_workload_sizes_sampled(orc, which):
             mode, dtype = WGRAD, torch.float32
     M, N = a.shape[0], b.shape[0]
     out = run_gpu(mode, a, sa, b, sb, dtype)
-    ms, ns = sample_positions(M, N, 4096, {"qkv_fprop": 1, "mlp_down_dgrad": 2, "mlp_down_wgrad": 3}[which])
+    ms, ns = sample_positions(M, N, 4096, {"qkv_fprop": 1, "mlp_down_dgrad": 2, "mlp_down_wgrad": 3,
+                                           "gate_up_wgrad": 4}[which])
     ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
     na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
     o = out_np(out)
