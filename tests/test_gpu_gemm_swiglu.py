@@ -158,10 +158,12 @@ def unfused(a, sa, b, sb):
     return to_np(q), to_np(s), bf16_bits_np(gu)
 
 
-@pytest.mark.parametrize("M,I,K", [(1000, 256, 528), (2600, 1024, 1040), (3000, 3072, 2048)])
+@pytest.mark.parametrize("M,I,K", [(1000, 256, 528), (2600, 1024, 1040), (3000, 3072, 752)])
 def test_fused_equals_unfused_pair(orc, M, I, K):
-    """Row-tile counts of 4, 11 and 12 (not multiples of 8) and ragged edges; the plain
-    fprop of these shapes runs without a split of its K loop, as the fused kernel does."""
+    """Row-tile counts of 4, 11 and 12 (not multiples of 8) and ragged edges; 288 work
+    items in the last case, so some workgroups take two.  The plain fprop of these shapes
+    runs without a split of its K loop, as the fused kernel does (at 6 K slices no split
+    is allowed)."""
     assert puro.puro_gemm_workspace_bytes(FPROP, M, 2 * I, K) == 0
     a, sa, b, sb = quantized_operands(orc, FPROP, M, 2 * I, K, 3 * M + I)
     for got, want, what in zip(run(a, sa, b, sb), unfused(a, sa, b, sb), ("codes", "scales", "gu")):
