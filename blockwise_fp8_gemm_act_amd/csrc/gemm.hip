@@ -930,13 +930,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   }
 }
 
-// Sum of the split-K partials in increasing split order (then added to the
-// fp32 output in accumulate mode).
-template <bool kBf16Out, bool kAcc = false>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, void *out, int64_t MN, int splits) {
-  static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += stride) {
+// out[i .. i+W-1] = the sum of the split-K partials ws[s*MN + i ..] in
+// increasing split order (then added to the fp32 output in accumulate mode);
+// W = 4 (16-byte loads) when kVec, else 1.
+template <bool kBf16Out, bool kAcc, bool kVec>
+__device__ __forceinline__ void reduce_at(const float *ws, void *out, int64_t i, int64_t MN, int splits) {
+  if constexpr (kVec) {
+    v4f v = *reinterpret_cast<const v4f *>(ws + i);
+    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const v4f *>(ws + (int64_t)s * MN + i);
+    if constexpr (kBf16Out) {
+      *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(out) + i) =
+          (u32x2){f32_to_bf16_rne(v[0]) | f32_to_bf16_rne(v[1]) << 16, f32_to_bf16_rne(v[2]) | f32_to_bf16_rne(v[3]) << 16};
+    } else {
+      v4f *o = reinterpret_cast<v4f *>(reinterpret_cast<float *>(out) + i);
+      if constexpr (kAcc) *o = *o + v;
+      else *o = v;
+    }
+  } else {
     float v = ws[i];
     for (int s = 1; s < splits; ++s) v += ws[(int64_t)s * MN + i];
     if constexpr (kBf16Out)
@@ -948,30 +958,36 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, voi
   }
 }
 
-// The same over the output tiles tile0 .. tile0 + ntiles - 1 only (the other
-// tiles were computed whole and stored directly): element e of the range is
-// row (e / 256) % 256, column e % 256 of tile tile0 + e / 65536.
-template <bool kBf16Out, bool kAcc = false>
+// The whole output (every tile split); kVec needs MN % 4 == 0.
+template <bool kBf16Out, bool kAcc, bool kVec>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *ws, void *out, int64_t MN, int splits) {
+  static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
+  constexpr int W = kVec ? 4 : 1;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < MN / W; e += stride)
+    reduce_at<kBf16Out, kAcc, kVec>(ws, out, e * W, MN, splits);
+}
+
+// The output tiles tile0 .. tile0 + ntiles - 1 only (the other tiles were
+// computed whole and stored directly): with W elements per thread, index e
+// covers row (e / (256/W)) % 256, columns W * (e % (256/W)) .. +W-1 of tile
+// tile0 + e / (65536/W).  kVec needs N % 4 == 0 (a group of 4 columns is then
+// either wholly inside the output or wholly past its last column).
+template <bool kBf16Out, bool kAcc, bool kVec>
 __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *ws, void *out, int64_t M, int64_t N,
                                                                   int tiles_m, int tile0, int ntiles, int splits) {
   static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
+  constexpr int W = kVec ? 4 : 1;
+  constexpr int kRowItems = kBN / W;
   const int64_t MN = M * N;
-  const int64_t total = (int64_t)ntiles * kBM * kBN;
+  const int64_t total = (int64_t)ntiles * kBM * kRowItems;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
-    const int tile = tile0 + (int)(e / (kBM * kBN));
-    const int r = (int)(e / kBN) % kBM, c = (int)(e % kBN);
+    const int tile = tile0 + (int)(e / (kBM * kRowItems));
+    const int r = (int)((e / kRowItems) % kBM), c = (int)(e % kRowItems) * W;
     const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * kBN + c;
     if (m >= M || n >= N) continue;
-    const int64_t i = m * N + n;
-    float v = ws[i];
-    for (int s = 1; s < splits; ++s) v += ws[(int64_t)s * MN + i];
-    if constexpr (kBf16Out)
-      reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)f32_to_bf16_rne(v);
-    else if constexpr (kAcc)
-      reinterpret_cast<float *>(out)[i] += v;
-    else
-      reinterpret_cast<float *>(out)[i] = v;
+    reduce_at<kBf16Out, kAcc, kVec>(ws, out, m * N + n, MN, splits);
   }
 }
 
@@ -1108,30 +1124,27 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   const bool to_ws = p.splits > 1;
   err = launch(p.whole, tiles - p.whole, p.splits, p.spl, to_ws);
   if (err != hipSuccess || !to_ws) return err;
-  if (p.whole > 0) {
-    const int64_t n = (int64_t)(tiles - p.whole) * kBM * kBN;
-    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
-    const float *w = (const float *)ws;
-    const int nt = tiles - p.whole;
-    if (bf16_out)
-      hipLaunchKernelGGL(splitk_reduce_tiles_kernel<true>, dim3(blocks), dim3(256), 0, stream, w, out, M, N, p.tiles_m,
-                         p.whole, nt, p.splits);
-    else if (accumulate)
-      hipLaunchKernelGGL((splitk_reduce_tiles_kernel<false, true>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
+  const float *w = (const float *)ws;
+  const int nt = tiles - p.whole;
+  auto reduce = [&](auto bf16_c, auto acc_c, auto vec_c) {
+    constexpr bool kB = decltype(bf16_c)::value, kA = decltype(acc_c)::value, kV = decltype(vec_c)::value;
+    constexpr int W = kV ? 4 : 1;
+    if (p.whole > 0) {
+      const int64_t n = (int64_t)nt * kBM * kBN / W;
+      const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
+      hipLaunchKernelGGL((splitk_reduce_tiles_kernel<kB, kA, kV>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
                          p.tiles_m, p.whole, nt, p.splits);
-    else
-      hipLaunchKernelGGL(splitk_reduce_tiles_kernel<false>, dim3(blocks), dim3(256), 0, stream, w, out, M, N, p.tiles_m,
-                         p.whole, nt, p.splits);
-    return hipGetLastError();
-  }
-  const int blocks = (int)std::min<int64_t>((MN + 255) / 256, 8192);
-  if (bf16_out)
-    hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
-  else if (accumulate)
-    hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN,
-                       p.splits);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(blocks), dim3(256), 0, stream, (const float *)ws, out, MN, p.splits);
+    } else {
+      const int blocks = (int)std::min<int64_t>((MN / W + 255) / 256, 8192);
+      hipLaunchKernelGGL((splitk_reduce_kernel<kB, kA, kV>), dim3(blocks), dim3(256), 0, stream, w, out, MN, p.splits);
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  const bool vec = p.whole > 0 ? (N % 4 == 0) : (MN % 4 == 0);
+  if (bf16_out) vec ? reduce(T{}, F{}, T{}) : reduce(T{}, F{}, F{});
+  else if (accumulate) vec ? reduce(F{}, T{}, T{}) : reduce(F{}, T{}, F{});
+  else vec ? reduce(F{}, F{}, T{}) : reduce(F{}, F{}, F{});
   return hipGetLastError();
 }
 

@@ -90,8 +90,11 @@ def test_ragged_shapes(orc, mode, M, N, K, dtype):
 
 
 @pytest.mark.parametrize("mode", [FPROP, WGRAD])
-def test_split_k_path(orc, mode):
-    M, N, K = 512, 512, 4096
+@pytest.mark.parametrize("M,N", [(512, 512), (510, 511)])
+def test_split_k_path(orc, mode, M, N):
+    """Every tile split over K; the reduction reads 4 partials per thread when M * N is a
+    multiple of 4, one otherwise (510 x 511)."""
+    K = 4096
     assert puro.puro_gemm_workspace_bytes(mode, M, N, K) > 0
     a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=99)
     for dtype in (torch.float32, torch.bfloat16):
@@ -122,11 +125,13 @@ def whole_then_split_check(orc, mode, a, sa, b, sb, out, dtype, what):
 
 
 @pytest.mark.parametrize("mode", [FPROP, WGRAD])
-def test_whole_tiles_then_split_remainder(orc, mode):
+@pytest.mark.parametrize("N", [10900, 10899])
+def test_whole_tiles_then_split_remainder(orc, mode, N):
     """258 output tiles (6 x 43) at 8 K slices: tiles 0-255 fill the compute units once and run whole in a
     first launch; only the last two, ragged in rows, columns and K, are split over K by a second launch and
-    summed by the tile-range reduction.  fp32 and bf16 out; two calls give the same bits."""
-    M, N, K = 1480, 10900, 1008
+    summed by the tile-range reduction (4 columns per thread when N is a multiple of 4, else one).  fp32 and
+    bf16 out; two calls give the same bits."""
+    M, K = 1480, 1008
     assert puro.puro_gemm_workspace_bytes(mode, M, N, K) > 0
     a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=258)
     for dtype in (torch.float32, torch.bfloat16):
