@@ -13,7 +13,10 @@ One step = one pass of the whole path over one Qwen3-1.7B-shaped layer
   - wgrad  dW = dY^T X    (fp32 out, contracting over the tokens).
 Inputs are seeded synthetic tensors (see workloads.py) resident in HBM before
 the timed region.  The reported value is GEMM TFLOP/s over the whole step
-(quantizers included in the time).
+(quantizers included in the time).  The timed steps record HIP events only at
+their two ends; the per-launch table (and the roofline of a workload of several
+kernel kinds) comes from as many further steps with an event between
+consecutive launches.
 
 Other workloads (--workload):
   layer_fp8_saved  the same layer step when the forward pass keeps only the
@@ -506,10 +509,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # Events between launches cost a few microseconds each on the GPU timeline.
-    # A workload of a single kernel kind is timed without them (its roofline
-    # is then total algorithmic bytes over the step time), and its per-launch
-    # table comes from one extra untimed step with events.
+    # Events between launches cost a few microseconds each on the GPU timeline
+    # (about 0.08 ms over the layer step's 25).  The K timed steps therefore
+    # carry events only at their two ends and give `value` and ms_per_step.
+    # The per-launch durations come from events between consecutive launches:
+    # over K more steps right after the timed ones for a workload of several
+    # kernel kinds (its roofline uses them), over one more step for a single
+    # kind (its roofline is total algorithmic work over the step time).
     single_kind = len({l.kind for l in launches}) == 1
     n_ev = 1 if single_kind else args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(n_ev)]
@@ -519,15 +525,15 @@ def main():
     t0 = time.perf_counter()
     start.record()
     for s in range(args.steps):
-        step(None if single_kind else ev[s])
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
-    if single_kind:
-        step(ev[0])
-        torch.cuda.synchronize()
+    for s in range(n_ev):
+        step(ev[s])
+    torch.cuda.synchronize()
 
     # per-launch durations (event before this launch -> event before the next)
     per = {}
@@ -584,8 +590,9 @@ def main():
                                       else round(dom["bytes"] / dom["launches"] / 1e6, 3))
     roof["algorithmic_unit"] = "GFLOP" if dom_kind.startswith("gemm") else "MB"
     roof["avg_launch_ms"] = round(dom["ms"] / dom["launches"], 4)
-    roof["timing"] = ("HIP events around each timed step, no events between its launches" if single_kind
-                      else "HIP events between consecutive launches of each timed step")
+    roof["timing"] = ("HIP events around the timed steps, no events between their launches" if single_kind
+                      else "HIP events between consecutive launches over %d steps run right after the %d timed steps "
+                           "(which carry no events between launches)" % (n_ev, args.steps))
     tr = load_traffic(dom_kind)
     roof["traffic"] = tr
 
