@@ -19,6 +19,7 @@ current stream.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -141,6 +142,23 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
+def _on_stream(fn):
+    """The helpers below allocate their outputs (and the GEMM's workspace) with torch's
+    caching allocator.  Given an explicit `stream`, the helper runs with it as torch's
+    current stream, so that those allocations belong to the stream the kernels are
+    enqueued on: freeing one then cannot hand its memory to other work before the
+    kernels that use it have finished.  `stream` is a torch.cuda.Stream or a raw
+    hipStream_t handle."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        ts = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(ts):
+            return fn(*args, **kw)
+    return run
+
+
 def _check(status: int, call: str):
     if status != PURO_OK:
         raise PuroError(status, call)
@@ -193,6 +211,7 @@ def _gemm_operands(mode: int, a, sa, b, sb):
     return M, N, K, dev
 
 
+@_on_stream
 def quant_act_1x128(x: torch.Tensor, q=None, s=None, stream=None):
     """1x128 tiles: returns (q uint8 [R][C], s fp32 [ceil(C/128)][R])."""
     _bf16_input(x, "x")
@@ -206,6 +225,7 @@ def quant_act_1x128(x: torch.Tensor, q=None, s=None, stream=None):
     return q, s
 
 
+@_on_stream
 def quant_w_128x128(w: torch.Tensor, q=None, s=None, stream=None):
     """128x128 blocks: returns (q uint8 [R][C], s fp32 [ceil(R/128)][ceil(C/128)])."""
     _bf16_input(w, "w")
@@ -219,6 +239,7 @@ def quant_w_128x128(w: torch.Tensor, q=None, s=None, stream=None):
     return q, s
 
 
+@_on_stream
 def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None):
     """Transposed quantization.  Returns (qt, st) or (qt, st, q_row, s_row) when dual.
 
@@ -245,6 +266,7 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
     return (qt, st, q, s) if dual else (qt, st)
 
 
+@_on_stream
 def quant_act_128x1(x: torch.Tensor, dual: bool = False, stream=None):
     """128x1 tiles with the codes in x's own layout: returns (qc uint8 [R][C], sc fp32
     [ceil(R/128)][C]), plus (q, s) as quant_act_1x128 when dual."""
@@ -263,6 +285,7 @@ def quant_act_128x1(x: torch.Tensor, dual: bool = False, stream=None):
     return (qc, sc, q, s) if dual else (qc, sc)
 
 
+@_on_stream
 def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=None):
     """Saved 1x128 codes q uint8 [R][C] and scales s fp32 [ceil(C/128)][R] ->
     (qt uint8 [C][R], st fp32 [ceil(R/128)][C]) in transposed 128x1 tiles."""
@@ -280,6 +303,7 @@ def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=Non
     return qt, st
 
 
+@_on_stream
 def swiglu_quant(gu: torch.Tensor, dual: bool = False, write_h: bool = False, stream=None):
     """SwiGLU of a [R][2I] gate/up bf16 tensor (gate first) fused with quantization of
     h = bf16(silu(gate) * up).  Returns (q, s) [+ (qt, st) when dual] [+ h when write_h]."""
@@ -313,6 +337,7 @@ def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):
     return torch.empty((max(n, 16),), dtype=torch.uint8, device=device), n
 
 
+@_on_stream
 def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=None, workspace=None,
                        stream=None):
     """out[m][n] = sum_k deq(a)[m][k] * deq(b)[n][k]; a [M][K], b [N][K] uint8 codes
@@ -338,6 +363,7 @@ def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=No
     return out
 
 
+@_on_stream
 def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, workspace=None, stream=None):
     """out (fp32 [M][N]) += the blockwise-scaled FP8 GEMM of a [M][K] and b [N][K]; returns out.
     Scale layouts as for gemm_fp8_blockwise."""
@@ -356,6 +382,7 @@ def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, wo
     return out
 
 
+@_on_stream
 def gemm_fp8_swiglu_quant(a, sa, b, sb, write_gu: bool = True, stream=None):
     """Fprop of a fused gate/up projection with the SwiGLU quantizer as its epilogue.
     a [M][K] codes, sa [ceil(K/128)][M]; b [2I][K] codes (gate rows, then up rows),
