@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from helpers import assert_codes_equal, assert_scales_equal, cdiv, to_np, TILE
-from workloads import bits, make, random_bf16
+from workloads import LINEARS, bits, make, random_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -134,6 +134,15 @@ def test_empty_inputs_enqueue_nothing():
     q, s = puro.quant_w_128x128(x)
     assert q.shape == (64, 0)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", [f"{k}_{lin}" for lin in LINEARS for k in ("x", "w", "dy")])
+def test_layer_tensors_in_bench_form(orc, name):
+    """Each of the layer step's 12 quantizations at 16384 tokens, in the form the benchmark
+    runs it: the dual transposed quantizer (ACT for inputs and output gradients, WEIGHT for
+    weights), codes and scales of both outputs bit-exact."""
+    t = make("layer", names={name})[name]
+    check_t(orc, puro.T_WEIGHT if name.startswith("w_") else puro.T_ACT, t, dual=True)
 
 
 def test_workload_sizes(orc):
