@@ -82,9 +82,11 @@ def test_w_128x128(orc, R, C):
     check_w(orc, special_input(R, C, R + 7))
 
 
-@pytest.mark.parametrize("R,C", [(256, 384), (144, 80), (16, 16), (1024, 2064)])
+@pytest.mark.parametrize("R,C", [(256, 384), (144, 80), (16, 16), (1024, 2064),
+                                 (16, 4096), (144, 4112), (400, 4096), (768, 6144)])
 @pytest.mark.parametrize("dual", [False, True])
 def test_transpose_act(orc, R, C, dual):
+    """Ragged rows and columns, from a single 16-row block to inputs 4096-6144 wide."""
     check_t(orc, puro.T_ACT, outlier_input(R, C, R + 2 * C), dual)
     check_t(orc, puro.T_ACT, special_input(R, C, R + 5), dual)
 

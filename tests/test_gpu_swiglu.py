@@ -39,7 +39,7 @@ def gate_up(R, I, seed, std=1.0):
     return (torch.randn((R, 2 * I), generator=g) * std).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("R,I", [(256, 256), (144, 80), (16, 16), (1040, 400), (512, 2048)])
+@pytest.mark.parametrize("R,I", [(256, 256), (144, 80), (16, 16), (1040, 400), (512, 2048), (400, 4096), (16, 4112)])
 @pytest.mark.parametrize("dual", [False, True])
 def test_random_gate_up(orc, R, I, dual):
     check(orc, gate_up(R, I, R + I), dual)
