@@ -254,6 +254,18 @@ def test_gemm_workspace_sizing():
     # a split-K shape has fp32 partials for every split
     n = ws(2, 2048, 2048, 16384)
     assert n > 0 and n % (2048 * 2048 * 4) == 0
+    # the layer's split wgrads at 16384 tokens: qkv in 2, o in 4, gate_up (256 tiles whole, the
+    # other 128 in 2; the workspace keeps the full [splits][M][N] layout), down unsplit
+    assert ws(2, 4096, 2048, 16384) == 2 * 4096 * 2048 * 4
+    assert ws(2, 2048, 2048, 16384) == 4 * 2048 * 2048 * 4
+    assert ws(2, 12288, 2048, 16384) == 2 * 12288 * 2048 * 4
+    assert ws(2, 2048, 6144, 16384) == 0
+    # 258 tiles at 8 K slices: whole tiles first, the last two split in 2
+    assert ws(0, 1480, 10900, 1008) == 2 * 1480 * 10900 * 4
+    # the fprop and dgrad shapes of the layer never split
+    for M, N, K in [(16384, 4096, 2048), (16384, 2048, 2048), (16384, 12288, 2048), (16384, 2048, 6144),
+                    (16384, 2048, 4096), (16384, 2048, 12288), (16384, 6144, 2048)]:
+        assert ws(0, M, N, K) == 0 and ws(1, M, N, K) == 0
 
 
 def test_gemm_workspace_errors():
