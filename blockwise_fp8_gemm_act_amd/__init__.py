@@ -71,6 +71,17 @@ _lib.puro_abi_version.argtypes = []
 _lib.puro_abi_version.restype = ctypes.c_int
 
 
+def _torch_empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+# Allocator of every output and workspace buffer the tensor helpers create.  It is
+# a module attribute so that a test harness can substitute one that fills new
+# buffers with a poison value: a kernel that skips part of its output then leaves
+# the poison in place instead of whatever the caching allocator's memory held.
+empty = _torch_empty
+
+
 class PuroError(RuntimeError):
     def __init__(self, status: int, call: str):
         self.status = status
@@ -216,8 +227,8 @@ def quant_act_1x128(x: torch.Tensor, q=None, s=None, stream=None):
     """1x128 tiles: returns (q uint8 [R][C], s fp32 [ceil(C/128)][R])."""
     _bf16_input(x, "x")
     R, C = x.shape
-    q = torch.empty((R, C), dtype=torch.uint8, device=x.device) if q is None else q
-    s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device) if s is None else s
+    q = empty((R, C), dtype=torch.uint8, device=x.device) if q is None else q
+    s = empty((_cdiv(C, TILE), R), dtype=torch.float32, device=x.device) if s is None else s
     _tensor(q, "q", torch.uint8, (R, C), x.device)
     _tensor(s, "s", torch.float32, (_cdiv(C, TILE), R), x.device)
     _check(puro_quant_act_1x128(x.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
@@ -230,8 +241,8 @@ def quant_w_128x128(w: torch.Tensor, q=None, s=None, stream=None):
     """128x128 blocks: returns (q uint8 [R][C], s fp32 [ceil(R/128)][ceil(C/128)])."""
     _bf16_input(w, "w")
     R, C = w.shape
-    q = torch.empty((R, C), dtype=torch.uint8, device=w.device) if q is None else q
-    s = torch.empty((_cdiv(R, TILE), _cdiv(C, TILE)), dtype=torch.float32, device=w.device) if s is None else s
+    q = empty((R, C), dtype=torch.uint8, device=w.device) if q is None else q
+    s = empty((_cdiv(R, TILE), _cdiv(C, TILE)), dtype=torch.float32, device=w.device) if s is None else s
     _tensor(q, "q", torch.uint8, (R, C), w.device)
     _tensor(s, "s", torch.float32, (_cdiv(R, TILE), _cdiv(C, TILE)), w.device)
     _check(puro_quant_w_128x128(w.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), _stream(stream)),
@@ -249,17 +260,17 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
     _bf16_input(x, "x")
     R, C = x.shape
     dev = x.device
-    qt = torch.empty((C, R), dtype=torch.uint8, device=dev)
+    qt = empty((C, R), dtype=torch.uint8, device=dev)
     if kind == T_ACT:
-        st = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
+        st = empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
         s_shape = (_cdiv(C, TILE), R)
     else:
-        st = torch.empty((_cdiv(C, TILE), _cdiv(R, TILE)), dtype=torch.float32, device=dev)
+        st = empty((_cdiv(C, TILE), _cdiv(R, TILE)), dtype=torch.float32, device=dev)
         s_shape = (_cdiv(R, TILE), _cdiv(C, TILE))
     q = s = None
     if dual:
-        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
-        s = torch.empty(s_shape, dtype=torch.float32, device=dev)
+        q = empty((R, C), dtype=torch.uint8, device=dev)
+        s = empty(s_shape, dtype=torch.float32, device=dev)
     _check(puro_quant_transpose(kind, x.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
                                 q.data_ptr() if dual else None, s.data_ptr() if dual else None,
                                 _stream(stream)), "puro_quant_transpose")
@@ -273,12 +284,12 @@ def quant_act_128x1(x: torch.Tensor, dual: bool = False, stream=None):
     _bf16_input(x, "x")
     R, C = x.shape
     dev = x.device
-    qc = torch.empty((R, C), dtype=torch.uint8, device=dev)
-    sc = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
+    qc = empty((R, C), dtype=torch.uint8, device=dev)
+    sc = empty((_cdiv(R, TILE), C), dtype=torch.float32, device=dev)
     q = s = None
     if dual:
-        q = torch.empty((R, C), dtype=torch.uint8, device=dev)
-        s = torch.empty((_cdiv(C, TILE), R), dtype=torch.float32, device=dev)
+        q = empty((R, C), dtype=torch.uint8, device=dev)
+        s = empty((_cdiv(C, TILE), R), dtype=torch.float32, device=dev)
     _check(puro_quant_act_128x1(x.data_ptr(), R, C, qc.data_ptr(), sc.data_ptr(),
                                 q.data_ptr() if dual else None, s.data_ptr() if dual else None, _stream(stream)),
            "puro_quant_act_128x1")
@@ -294,8 +305,8 @@ def requant_act_t(q: torch.Tensor, s: torch.Tensor, qt=None, st=None, stream=Non
     R, C = q.shape
     _tensor(q, "q", torch.uint8, (R, C))
     _tensor(s, "s", torch.float32, (_cdiv(C, TILE), R), q.device)
-    qt = torch.empty((C, R), dtype=torch.uint8, device=q.device) if qt is None else qt
-    st = torch.empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device) if st is None else st
+    qt = empty((C, R), dtype=torch.uint8, device=q.device) if qt is None else qt
+    st = empty((_cdiv(R, TILE), C), dtype=torch.float32, device=q.device) if st is None else st
     _tensor(qt, "qt", torch.uint8, (C, R), q.device)
     _tensor(st, "st", torch.float32, (_cdiv(R, TILE), C), q.device)
     _check(puro_requant_act_t(q.data_ptr(), s.data_ptr(), R, C, qt.data_ptr(), st.data_ptr(),
@@ -313,14 +324,14 @@ def swiglu_quant(gu: torch.Tensor, dual: bool = False, write_h: bool = False, st
         raise ValueError("gu needs an even number of columns (gate then up)")
     I = C2 // 2
     dev = gu.device
-    q = torch.empty((R, I), dtype=torch.uint8, device=dev)
-    s = torch.empty((_cdiv(I, TILE), R), dtype=torch.float32, device=dev)
+    q = empty((R, I), dtype=torch.uint8, device=dev)
+    s = empty((_cdiv(I, TILE), R), dtype=torch.float32, device=dev)
     qt = st = h = None
     if dual:
-        qt = torch.empty((I, R), dtype=torch.uint8, device=dev)
-        st = torch.empty((_cdiv(R, TILE), I), dtype=torch.float32, device=dev)
+        qt = empty((I, R), dtype=torch.uint8, device=dev)
+        st = empty((_cdiv(R, TILE), I), dtype=torch.float32, device=dev)
     if write_h:
-        h = torch.empty((R, I), dtype=torch.bfloat16, device=dev)
+        h = empty((R, I), dtype=torch.bfloat16, device=dev)
     _check(puro_swiglu_quant(gu.data_ptr(), R, I, q.data_ptr(), s.data_ptr(),
                              qt.data_ptr() if dual else None, st.data_ptr() if dual else None,
                              h.data_ptr() if write_h else None, _stream(stream)), "puro_swiglu_quant")
@@ -334,7 +345,7 @@ def swiglu_quant(gu: torch.Tensor, dual: bool = False, write_h: bool = False, st
 
 def gemm_workspace(mode: int, M: int, N: int, K: int, device="cuda"):
     n = puro_gemm_workspace_bytes(mode, M, N, K)
-    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device), n
+    return empty((max(n, 16),), dtype=torch.uint8, device=device), n
 
 
 @_on_stream
@@ -345,14 +356,14 @@ def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=No
     (FPROP, DGRAD) or [ceil(K/128)][N] (WGRAD, WGRAD_TM)."""
     M, N, K, dev = _gemm_operands(mode, a, sa, b, sb)
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=dev)
+        out = empty((M, N), dtype=out_dtype, device=dev)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     _tensor(out, "out", out.dtype, (M, N), dev)
     od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     need = puro_gemm_workspace_bytes(mode, M, N, K)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        workspace = empty((need,), dtype=torch.uint8, device=dev)
     if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev):
         raise ValueError("workspace must be a contiguous CUDA tensor on %s" % dev)
     wptr = workspace.data_ptr() if workspace is not None else None
@@ -371,7 +382,7 @@ def gemm_fp8_blockwise_accumulate(mode: int, a, sa, b, sb, out: torch.Tensor, wo
     _tensor(out, "out", torch.float32, (M, N), dev)
     need = puro_gemm_workspace_bytes(mode, M, N, K)
     if workspace is None and need > 0:
-        workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
+        workspace = empty((need,), dtype=torch.uint8, device=dev)
     if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != dev):
         raise ValueError("workspace must be a contiguous CUDA tensor on %s" % dev)
     wptr = workspace.data_ptr() if workspace is not None else None
@@ -392,9 +403,9 @@ def gemm_fp8_swiglu_quant(a, sa, b, sb, write_gu: bool = True, stream=None):
     if N % (2 * TILE):
         raise ValueError("b must have 2*I rows with I a multiple of 128")
     I = N // 2
-    hq = torch.empty((M, I), dtype=torch.uint8, device=dev)
-    hs = torch.empty((I // TILE, M), dtype=torch.float32, device=dev)
-    gu = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if write_gu else None
+    hq = empty((M, I), dtype=torch.uint8, device=dev)
+    hs = empty((I // TILE, M), dtype=torch.float32, device=dev)
+    gu = empty((M, N), dtype=torch.bfloat16, device=dev) if write_gu else None
     _check(puro_gemm_fp8_swiglu_quant(a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(), M, I, K,
                                       gu.data_ptr() if write_gu else None, hq.data_ptr(), hs.data_ptr(),
                                       _stream(stream)), "puro_gemm_fp8_swiglu_quant")

@@ -46,6 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "csrc", "device_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "csrc", "libdevprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The GPU tests' probe module (tests/csrc/device_probe.hip): device code of the
+    library exercised on its own.  Not part of the library."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-shared", PROBE_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for the probe module:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -58,6 +76,8 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    if os.path.exists(PROBE_SRC):
+        build_probe(verbose)
     return LIB
 
 

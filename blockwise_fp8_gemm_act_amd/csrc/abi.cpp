@@ -266,6 +266,7 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const
   return gemm_call(mode, a, sa, b, sb, out, out_dtype, false, M, N, K, workspace, workspace_bytes, stream);
 }
 
+
 puro_status puro_gemm_fp8_swiglu_quant(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                                        int64_t M, int64_t inter, int64_t K, uint16_t *gu, uint8_t *hq, float *hs,
                                        puro_stream_t stream) {

@@ -251,17 +251,22 @@ def test_gemm_workspace_sizing():
     # deterministic
     for shape in [(2, 2048, 6144, 8192), (2, 2048, 2048, 16384), (0, 256, 256, 8192)]:
         assert ws(*shape) == ws(*shape)
-    # a split-K shape has fp32 partials for every split
+    # a split-K shape has one 256 x 256 fp32 block per split of each split tile
+    tile = 256 * 256 * 4
     n = ws(2, 2048, 2048, 16384)
-    assert n > 0 and n % (2048 * 2048 * 4) == 0
-    # the layer's split wgrads at 16384 tokens: qkv in 2, o in 4, gate_up (256 tiles whole, the
-    # other 128 in 2; the workspace keeps the full [splits][M][N] layout), down unsplit
-    assert ws(2, 4096, 2048, 16384) == 2 * 4096 * 2048 * 4
-    assert ws(2, 2048, 2048, 16384) == 4 * 2048 * 2048 * 4
-    assert ws(2, 12288, 2048, 16384) == 2 * 12288 * 2048 * 4
+    assert n > 0 and n % tile == 0
+    # the layer's split wgrads at 16384 tokens: qkv (128 tiles) in 2, o (64 tiles) in 4, gate_up
+    # (384 tiles: 256 whole, the other 128 in 2), down unsplit
+    assert ws(2, 4096, 2048, 16384) == 2 * 128 * tile
+    assert ws(2, 2048, 2048, 16384) == 4 * 64 * tile
+    assert ws(2, 12288, 2048, 16384) == 2 * 128 * tile
     assert ws(2, 2048, 6144, 16384) == 0
-    # 258 tiles at 8 K slices: whole tiles first, the last two split in 2
-    assert ws(0, 1480, 10900, 1008) == 2 * 1480 * 10900 * 4
+    # none of them needs more than 64 MiB
+    assert max(ws(2, M, N, 16384) for M, N in [(4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)]) == 64 << 20
+    # 258 tiles (6 x 43) at 8 K slices: whole tiles first, the last two split in 2
+    assert ws(0, 1480, 10900, 1008) == 2 * 2 * tile
+    # ragged edge tiles take a whole block too
+    assert ws(2, 510, 511, 4096) % tile == 0
     # the fprop and dgrad shapes of the layer never split
     for M, N, K in [(16384, 4096, 2048), (16384, 2048, 2048), (16384, 12288, 2048), (16384, 2048, 6144),
                     (16384, 2048, 4096), (16384, 2048, 12288), (16384, 6144, 2048)]:

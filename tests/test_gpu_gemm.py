@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (DGRAD, FPROP, WGRAD, bf16_bits_np, cdiv, check_gemm_values,
+from helpers import (DGRAD, FPROP, WGRAD, bf16_bits_np, cdiv, check_gemm,
                      quantized_operands, to_np, TILE)
 from workloads import bits, make
 
@@ -30,28 +30,7 @@ def out_np(out):
 
 
 def check_full(orc, mode, a, sa, b, sb, dtype, what):
-    out = run_gpu(mode, a, sa, b, sb, dtype)
-    ref = orc.gemm(mode, a, sa, b, sb)
-    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
-    o = out_np(out)
-    ov = o if dtype == torch.float32 else out.float().cpu().numpy()
-    if dtype == torch.bfloat16:
-        return check_gemm_values_bf16(orc, o, ov, ref, na, nb, what)
-    return check_gemm_values(ov, ref, na[:, None], nb[None, :], False, orc, what)
-
-
-def check_gemm_values_bf16(orc, o16, ov, ref, na, nb, what):
-    denom = na[:, None] * nb[None, :]
-    err = np.abs(ov.astype(np.float64) - ref)
-    norm = np.where(denom > 0, err / np.where(denom > 0, denom, 1), np.where(err == 0, 0, np.inf))
-    from helpers import bf16_ordered, GEMM_TOL
-    ref16 = orc.f64_to_bf16_array(ref)
-    ulps = np.abs(bf16_ordered(o16) - bf16_ordered(ref16))
-    ok = (ulps <= 1) | (norm <= GEMM_TOL)
-    assert ok.all(), "%s: %d elements beyond 1 ulp and tolerance" % (what, int((~ok).sum()))
-    strict = float(np.mean(ulps <= 1))
-    print("%s: bf16 strictly within 1 ulp: %.7f (%d fallbacks)" % (what, strict, int((ulps > 1).sum())))
-    return float(norm.max()), strict
+    return check_gemm(orc, mode, a, sa, b, sb, run_gpu(mode, a, sa, b, sb, dtype), what)
 
 
 def test_tiny_fprop_workload_fp32(orc):
@@ -119,9 +98,7 @@ def whole_then_split_check(orc, mode, a, sa, b, sb, out, dtype, what):
     rm, rn = np.meshgrid(np.arange(1024, M), np.arange(10752, N), indexing="ij")
     sm, sn = sample_positions(M, N, 4096, M + N)
     ms, ns = np.concatenate([rm.ravel(), sm]), np.concatenate([rn.ravel(), sn])
-    ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
-    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
-    check_gemm_values(out_np(out)[ms, ns], ref, na[ms], nb[ns], dtype == torch.bfloat16, orc, what)
+    check_gemm(orc, mode, a, sa, b, sb, out, what, ms, ns)
 
 
 @pytest.mark.parametrize("mode", [FPROP, WGRAD])
@@ -205,18 +182,7 @@ def test_workload_sizes_sampled(orc, which):
     out = run_gpu(mode, a, sa, b, sb, dtype)
     ms, ns = sample_positions(M, N, 4096, {"qkv_fprop": 1, "mlp_down_dgrad": 2, "mlp_down_wgrad": 3,
                                            "gate_up_wgrad": 4}[which])
-    ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
-    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
-    o = out_np(out)
-    if dtype == torch.bfloat16:
-        ov = out.float().cpu().numpy()[ms, ns]
-        from helpers import bf16_ordered, GEMM_TOL
-        ref16 = orc.f64_to_bf16_array(ref)
-        ulps = np.abs(bf16_ordered(o[ms, ns]) - bf16_ordered(ref16))
-        norm = np.abs(ov - ref) / (na[ms] * nb[ns])
-        assert np.all((ulps <= 1) | (norm <= GEMM_TOL))
-    else:
-        check_gemm_values(o[ms, ns], ref, na[ms], nb[ns], False, orc, which)
+    check_gemm(orc, mode, a, sa, b, sb, out, which, ms, ns)
 
 
 def test_end_to_end_gpu_quantizers(orc):
@@ -229,9 +195,7 @@ def test_end_to_end_gpu_quantizers(orc):
     torch.cuda.synchronize()
     oa, osa = orc.quant_act_1x128(bits(t["x"]))
     ob, osb = orc.quant_w_128x128(bits(t["w"]))
-    ref = orc.gemm(FPROP, oa, osa, ob, osb)
-    na, nb = orc.deq_row_norms(FPROP, oa, osa, ob, osb)
-    check_gemm_values(to_np(out), ref, na[:, None], nb[None, :], False, orc, "end to end")
+    check_gemm(orc, FPROP, oa, osa, ob, osb, out, "end to end")
 
 
 def test_mfma_slice_accumulation_precision(orc):

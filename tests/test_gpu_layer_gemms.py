@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import DGRAD, FPROP, WGRAD, bf16_bits_np, check_gemm_values, to_np
+from helpers import DGRAD, FPROP, WGRAD, check_gemm
 from workloads import LINEARS, bits, make
 
 pytestmark = pytest.mark.gpu
@@ -36,10 +36,7 @@ def check(orc, mode, a, sa, b, sb, dtype, seed, what):
     rng = np.random.default_rng(seed)
     ms = np.concatenate([rng.integers(0, M, 2048), np.zeros(min(N, 512), np.int64), np.full(min(N, 512), M - 1)])
     ns = np.concatenate([rng.integers(0, N, 2048), np.arange(min(N, 512)), N - 1 - np.arange(min(N, 512))])
-    ref = orc.gemm_at(mode, a, sa, b, sb, ms, ns)
-    na, nb = orc.deq_row_norms(mode, a, sa, b, sb)
-    o = bf16_bits_np(out) if dtype == torch.bfloat16 else to_np(out)
-    check_gemm_values(o[ms, ns], ref, na[ms], nb[ns], dtype == torch.bfloat16, orc, what)
+    check_gemm(orc, mode, a, sa, b, sb, out, what, ms, ns)
 
 
 @pytest.mark.parametrize("op", ["fprop", "dgrad", "wgrad"])
