@@ -8,7 +8,8 @@ importing this package fails.
 
 The raw C calls keep their C names (``puro_quant_act_1x128``,
 ``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_requant_act_t``,
-``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_accumulate``,
+``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_noalloc``,
+``puro_gemm_fp8_blockwise_accumulate``,
 ``puro_gemm_fp8_swiglu_quant``, ...) and take integer device pointers.  The
 tensor-level helpers ``quant_act_1x128``, ``quant_w_128x128``,
 ``quant_transpose``, ``requant_act_t``, ``swiglu_quant``,
@@ -30,7 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libpuro.so")
 PURO_OK = 0
 STATUS_NAMES = {0: "PURO_OK", 1: "PURO_ERR_NULL", 2: "PURO_ERR_SHAPE", 3: "PURO_ERR_ALIGN",
                 4: "PURO_ERR_MODE", 5: "PURO_ERR_DTYPE", 6: "PURO_ERR_WORKSPACE",
-                7: "PURO_ERR_DEVICE", 8: "PURO_ERR_LAUNCH", 9: "PURO_ERR_ALIAS"}
+                7: "PURO_ERR_DEVICE", 8: "PURO_ERR_LAUNCH", 9: "PURO_ERR_ALIAS", 10: "PURO_ERR_SCRATCH"}
+SCRATCH_BYTES = 64 << 20       # device scratch of puro_gemm_fp8_blockwise_noalloc, per GPU
 FPROP, DGRAD, WGRAD, WGRAD_TM = 0, 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
 T_ACT, T_WEIGHT = 0, 1
@@ -60,6 +62,9 @@ _lib.puro_gemm_workspace_bytes.restype = ctypes.c_size_t
 _lib.puro_gemm_fp8_blockwise.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
                                          _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
 _lib.puro_gemm_fp8_blockwise.restype = ctypes.c_int
+_lib.puro_gemm_fp8_blockwise_noalloc.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int,
+                                                 _I64, _I64, _I64, _P]
+_lib.puro_gemm_fp8_blockwise_noalloc.restype = ctypes.c_int
 _lib.puro_gemm_fp8_blockwise_accumulate.argtypes = [ctypes.c_int, _P, _P, _P, _P, _P,
                                                     _I64, _I64, _I64, _P, ctypes.c_size_t, _P]
 _lib.puro_gemm_fp8_blockwise_accumulate.restype = ctypes.c_int
@@ -122,6 +127,10 @@ def puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspa
                             stream=None) -> int:
     return _lib.puro_gemm_fp8_blockwise(mode, a, sa, b, sb, out, out_dtype, M, N, K, workspace,
                                         workspace_bytes, stream)
+
+
+def puro_gemm_fp8_blockwise_noalloc(mode, a, sa, b, sb, out, out_dtype, M, N, K, stream=None) -> int:
+    return _lib.puro_gemm_fp8_blockwise_noalloc(mode, a, sa, b, sb, out, out_dtype, M, N, K, stream)
 
 
 def puro_gemm_fp8_blockwise_accumulate(mode, a, sa, b, sb, out, M, N, K, workspace, workspace_bytes,
@@ -371,6 +380,21 @@ def gemm_fp8_blockwise(mode: int, a, sa, b, sb, out_dtype=torch.bfloat16, out=No
     _check(puro_gemm_fp8_blockwise(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
                                    out.data_ptr(), od, M, N, K, wptr, wbytes, _stream(stream)),
            "puro_gemm_fp8_blockwise")
+    return out
+
+
+@_on_stream
+def gemm_fp8_blockwise_noalloc(mode: int, a, sa, b, sb, out: torch.Tensor, stream=None):
+    """gemm_fp8_blockwise into a caller's `out` (bf16 or fp32 [M][N]) with no allocation at
+    all: split-K partials go to the library's per-GPU device scratch.  Returns out."""
+    M, N, K, dev = _gemm_operands(mode, a, sa, b, sb)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _tensor(out, "out", out.dtype, (M, N), dev)
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    _check(puro_gemm_fp8_blockwise_noalloc(mode, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                                           out.data_ptr(), od, M, N, K, _stream(stream)),
+           "puro_gemm_fp8_blockwise_noalloc")
     return out
 
 

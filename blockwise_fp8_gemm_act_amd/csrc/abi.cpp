@@ -106,6 +106,7 @@ const char *puro_status_str(puro_status s) {
     case PURO_ERR_DEVICE: return "no current device, or the device is not gfx950";
     case PURO_ERR_LAUNCH: return "the HIP runtime failed to enqueue a kernel";
     case PURO_ERR_ALIAS: return "an output overlaps an input or another output";
+    case PURO_ERR_SCRATCH: return "the shape's split-K plan needs more than the library's 64 MiB device scratch";
   }
   return "unknown status";
 }
@@ -220,9 +221,10 @@ size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int6
 
 namespace {
 
+// noalloc: the split-K partials go to the library's scratch (workspace unused).
 puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                       void *out, puro_out_dtype out_dtype, bool accumulate, int64_t M, int64_t N, int64_t K,
-                      void *workspace, size_t workspace_bytes, puro_stream_t stream) {
+                      void *workspace, size_t workspace_bytes, puro_stream_t stream, bool noalloc = false) {
   if (mode != PURO_FPROP && mode != PURO_DGRAD && mode != PURO_WGRAD && mode != PURO_WGRAD_TM) return PURO_ERR_MODE;
   if (out_dtype != PURO_OUT_F32 && out_dtype != PURO_OUT_BF16) return PURO_ERR_DTYPE;
   if (!shape_ok(M, K) || !shape_ok(N, K) || !shape_ok(M, N) || K % 16 != 0 || K > kMaxGemmK)
@@ -237,7 +239,12 @@ puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, co
     plan = puro::plan_gemm((int)mode, M, N, K);
     if ((int64_t)plan.tiles_m * plan.tiles_n * plan.splits > kMaxDim) return PURO_ERR_SHAPE;
     if (!a || !sa || !b || !sb) return PURO_ERR_NULL;
-    if (plan.ws_bytes > 0 && !workspace) return PURO_ERR_WORKSPACE;
+    if (noalloc) {
+      if (plan.ws_bytes > puro::kScratchBytes) return PURO_ERR_SCRATCH;
+      plan.ws_bytes = 0;                     // no caller workspace to check
+    } else if (plan.ws_bytes > 0 && !workspace) {
+      return PURO_ERR_WORKSPACE;
+    }
   }
   if (!aligned16(out)) return PURO_ERR_ALIGN;
   if (K > 0) {
@@ -251,6 +258,9 @@ puro_status gemm_call(puro_gemm_mode mode, const uint8_t *a, const float *sa, co
     if (plan.ws_bytes > 0 && workspace_bytes < plan.ws_bytes) return PURO_ERR_WORKSPACE;
   }
   if (puro_status d = check_device()) return d;
+  if (noalloc)
+    return launched(puro::run_gemm_noalloc((int)mode, a, sa, b, sb, out, out_dtype == PURO_OUT_BF16, M, N, K,
+                                           (hipStream_t)stream));
   return launched(puro::run_gemm((int)mode, a, sa, b, sb, out, out_dtype == PURO_OUT_BF16, accumulate, M, N, K,
                                  workspace, (hipStream_t)stream));
 }
@@ -266,6 +276,12 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode, const uint8_t *a, const
   return gemm_call(mode, a, sa, b, sb, out, out_dtype, false, M, N, K, workspace, workspace_bytes, stream);
 }
 
+puro_status puro_gemm_fp8_blockwise_noalloc(puro_gemm_mode mode, const uint8_t *a, const float *sa,
+                                            const uint8_t *b, const float *sb, void *out,
+                                            puro_out_dtype out_dtype, int64_t M, int64_t N, int64_t K,
+                                            puro_stream_t stream) {
+  return gemm_call(mode, a, sa, b, sb, out, out_dtype, false, M, N, K, nullptr, 0, stream, true);
+}
 
 puro_status puro_gemm_fp8_swiglu_quant(const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
                                        int64_t M, int64_t inter, int64_t K, uint16_t *gu, uint8_t *hq, float *hs,

@@ -1155,6 +1155,46 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- allocation-free entry
+
+// Split-K scratch of run_gemm_noalloc: device memory owned by the library, one
+// copy per GPU (each device that loads the library holds it until the process
+// ends).  kScratchBytes is the largest workspace any GEMM of the layer at 16384
+// tokens plans.  In host code `scratch` only names the symbol: its device
+// address comes from hipGetSymbolAddress, per device.
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (concurrent first calls store the same address).
+static hipError_t scratch_address(void **ptr) {
+  static std::atomic<void *> cached[64];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void *p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    cached[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
+hipError_t run_gemm_noalloc(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                            void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  void *ws = nullptr;
+  if (K > 0 && plan_gemm(mode, M, N, K).ws_bytes > 0) {
+    if (plan_gemm(mode, M, N, K).ws_bytes > kScratchBytes) return hipErrorInvalidValue;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+  }
+  return run_gemm(mode, a, sa, b, sb, out, bf16_out, false, M, N, K, ws, stream);
+}
+
 // Fused gate/up fprop + SwiGLU + 1x128 quantizer.  One work item per 256
 // rows x 128 h columns (its 128 gate and 128 up rows of B); no split-K.  The
 // results are those of the bf16 fprop followed by the SwiGLU quantizer.

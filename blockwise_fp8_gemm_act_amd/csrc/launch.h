@@ -42,6 +42,15 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
                     void *out, bool bf16_out, bool accumulate, int64_t M, int64_t N, int64_t K, void *ws,
                     hipStream_t stream);
 
+// The GEMM with its split-K partials in the library's own device scratch
+// (kScratchBytes, one per device) instead of a caller's workspace: no device
+// allocation.  Shapes whose plan needs more scratch are refused
+// (hipErrorInvalidValue; the ABI layer checks this first).  Calls that overlap
+// on one device share the scratch and race.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t run_gemm_noalloc(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
+                            void *out, bool bf16_out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
 // Fused fprop of a gate/up projection (B = [gate rows; up rows], 2I x K,
 // 128x128 block scales) with the SwiGLU quantizer as its epilogue: gu (bf16
 // [M][2I], optional), hq / hs (1x128 codes and scales of h).  I % 128 == 0.

@@ -54,7 +54,10 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 6
+#define PURO_ABI_VERSION 7
+
+/* Device scratch of puro_gemm_fp8_blockwise_noalloc, per GPU. */
+#define PURO_SCRATCH_BYTES (64ull << 20)
 
 typedef struct ihipStream_t *puro_stream_t;   /* = hipStream_t */
 
@@ -68,7 +71,9 @@ typedef enum {
     PURO_ERR_WORKSPACE = 6,   /* workspace missing or smaller than puro_gemm_workspace_bytes() */
     PURO_ERR_DEVICE = 7,      /* the current device is not gfx950, or no device */
     PURO_ERR_LAUNCH = 8,      /* the HIP runtime reported an error while enqueueing */
-    PURO_ERR_ALIAS = 9        /* an output overlaps an input or another output */
+    PURO_ERR_ALIAS = 9,       /* an output overlaps an input or another output */
+    PURO_ERR_SCRATCH = 10     /* puro_gemm_fp8_blockwise_noalloc: the shape needs more split-K
+                                 scratch than the library holds (PURO_SCRATCH_BYTES) */
 } puro_status;
 
 typedef enum {
@@ -223,6 +228,30 @@ puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode,
                                     int64_t M, int64_t N, int64_t K,
                                     void *workspace, size_t workspace_bytes,
                                     puro_stream_t stream);
+
+/*
+ * puro_gemm_fp8_blockwise_noalloc -- puro_gemm_fp8_blockwise without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  It allocates nothing: the split-K partials that a shape's plan
+ * needs go to a device scratch array the library holds, PURO_SCRATCH_BYTES
+ * (64 MiB) per GPU, from the first call on a device until the process ends.
+ * Same arguments, results and errors as puro_gemm_fp8_blockwise with the same
+ * shape (the same plan and kernels: the output is bit for bit the same), plus:
+ *   PURO_ERR_SCRATCH  the shape's plan needs more than PURO_SCRATCH_BYTES of
+ *                     partials (puro_gemm_workspace_bytes(mode, M, N, K) tells
+ *                     how much); every GEMM of the layer at 16384 tokens fits.
+ * Every call on one GPU uses that GPU's single scratch array: calls that can
+ * run at the same time on one GPU (other streams, other host threads) race and
+ * must be serialized by the caller.  The scratch needs no clearing: every
+ * partial is written before it is read.
+ */
+puro_status puro_gemm_fp8_blockwise_noalloc(puro_gemm_mode mode,
+                                            const uint8_t *a, const float *sa,
+                                            const uint8_t *b, const float *sb,
+                                            void *out, puro_out_dtype out_dtype,
+                                            int64_t M, int64_t N, int64_t K,
+                                            puro_stream_t stream);
 
 /*
  * puro_gemm_fp8_blockwise_accumulate -- the same GEMM, added into an fp32

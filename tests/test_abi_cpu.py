@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "puro.h")
 
 import blockwise_fp8_gemm_act_amd as puro  # noqa: E402
 
-OK, NULL, SHAPE, ALIGN, MODE, DTYPE, WS, DEVICE, LAUNCH, ALIAS = range(10)
+OK, NULL, SHAPE, ALIGN, MODE, DTYPE, WS, DEVICE, LAUNCH, ALIAS, SCRATCH = range(11)
 
 # fake, 16-byte aligned, well separated device addresses (never dereferenced)
 A0, A1, A2, A3, A4, A5, A6 = (0x7F0000000000 + i * (1 << 32) for i in range(7))
@@ -28,6 +28,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose", "puro_quant_act_128x1",
                             "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
+                            "puro_gemm_fp8_blockwise_noalloc",
                             "puro_gemm_fp8_blockwise_accumulate", "puro_gemm_fp8_swiglu_quant",
                             "puro_status_str", "puro_abi_version"])
 
@@ -42,8 +43,8 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 6
-    for s in range(10):
+    assert puro.puro_abi_version() == 7
+    for s in range(11):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
 
@@ -284,6 +285,26 @@ def test_gemm_workspace_errors():
     assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A4 + 16, need) == ALIAS
     if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
         assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5, need) == DEVICE
+
+
+def test_gemm_noalloc_validation():
+    """The allocation-free GEMM validates like the workspace one, without a workspace, and
+    refuses shapes whose split-K plan needs more than the library's 64 MiB scratch."""
+    f = puro.puro_gemm_fp8_blockwise_noalloc
+    assert f(7, A0, A1, A2, A3, A4, 0, 256, 256, 256) == MODE
+    assert f(0, A0, A1, A2, A3, A4, 5, 256, 256, 256) == DTYPE
+    assert f(0, A0, A1, A2, A3, A4, 0, 256, 256, 100) == SHAPE
+    assert f(0, None, A1, A2, A3, A4, 0, 256, 256, 256) == NULL
+    assert f(0, A0 + 4, A1, A2, A3, A4, 0, 256, 256, 256) == ALIGN
+    assert f(0, A0, A1, A2, A3, A0, 0, 256, 256, 256) == ALIAS
+    assert puro.puro_gemm_workspace_bytes(2, 2560, 2560, 1 << 20) > puro.SCRATCH_BYTES
+    assert f(2, A0, A1, A2, A3, A4, 0, 2560, 2560, 1 << 20) == SCRATCH
+    assert f(0, A0, A1, A2, A3, A4, 0, 0, 256, 256) == OK           # empty output: nothing to do
+    if no_gpu():
+        # the layer's largest split plans fit the scratch; valid calls stop at the device check
+        for M, N in [(4096, 2048), (2048, 2048), (12288, 2048)]:
+            assert 0 < puro.puro_gemm_workspace_bytes(2, M, N, 16384) <= puro.SCRATCH_BYTES
+            assert f(2, A0, A1, A2, A3, A4, 0, M, N, 16384) == DEVICE
 
 
 def test_tensor_helpers_reject_host_tensors_and_bad_modes():
