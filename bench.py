@@ -33,8 +33,16 @@ Other workloads (--workload):
                    projection's two operands out): HBM GB/s;
   qkv_fprop, mlp_fprop, mlp_down_bwd   single GEMM slices of the layer.
 
+The default layer run also reports, in its `configs` block, the four smaller
+workloads measured in the same invocation (tiny fprop, QKV fprop at 4096 tokens,
+MLP fprop and MLP down backward at 8192 tokens), each with its quantizers and
+GEMMs: ms per step, TFLOP/s and % of the FP8 peak, quantizer GB/s and % of HBM.
+Every workload whose buffers (inputs, outputs, workspaces) come to less than
+512 MB rotates over as many copies of them as it takes to exceed 512 MB, twice
+the 256 MB of L2 and MALL.
+
 Prints ONE JSON line.  Options: --steps K --warmup W (defaults 30 / 10 for the
-layer workloads, 300 / 300 for the single-kernel ones),
+layer workloads, 300 / 300 for the single-kernel ones), --no-configs,
 --gpus N (only 1 is supported: the path is measured on one GPU),
 --workload NAME, --no-cpu-baseline.
 """
@@ -76,6 +84,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="layer workload: skip the per-config lines of the smaller workloads")
+    ap.add_argument("--config-steps", type=int, default=50,
+                    help="warm-up and timed steps of each smaller workload in the configs block")
     args = ap.parse_args()
     # A single-kernel step lasts ~0.1 ms: a few hundred untimed steps first let the
     # clocks settle (5 of them left the fused SwiGLU kernel ~10% slower), and the
@@ -266,6 +278,10 @@ def build_plan(workload, tensors, puro, torch):
             requant((q, s), lin + ".requant_x")
     elif workload == "swiglu_quant":
         swiglu(tensors["gu"], "down.swiglu_quant")
+    elif workload == "tiny_fprop":
+        xrow = q_act(tensors["x"], "quant_x")
+        wrow, _ = q_w_dual(tensors["w"], "quant_w", transposed=False)
+        gemm(puro.FPROP, xrow, wrow, torch.float32, "fprop")
     elif workload == "qkv_fprop":
         xrow = q_act(tensors["x"], "quant_x")
         wrow, _ = q_w_dual(tensors["w"], "quant_w", transposed=False)
@@ -306,6 +322,7 @@ WORKLOAD_DESC = {
                 "X_qkv, X_o, X_gate_up [16384x2048], X_down [16384x6144]"),
     "swiglu_quant": ("fused SwiGLU of the MLP gate/up output [16384x12288] (gate first) with 1x128 and 128x1 "
                      "quantization of h [16384x6144], the down projection's fprop and wgrad operands"),
+    "tiny_fprop": "tiny fprop: X[256x256] (2 outlier channels) x W[512x256]^T -> fp32, quantizers included",
     "qkv_fprop": "QKV projection fprop, 4096 tokens: X[4096x2048] x W[4096x2048]^T -> bf16",
     "mlp_fprop": "MLP fprop, 8192 tokens: gate_up X[8192x2048] x W[12288x2048]^T, down X[8192x6144] x W[2048x6144]^T",
     "mlp_down_bwd": "MLP down backward, 8192 tokens: dgrad dY[8192x2048] x W[2048x6144], wgrad dY^T x X[8192x6144]",
@@ -465,6 +482,106 @@ def cpu_baseline(tensors, workload, budget_s):
     }
 
 
+def time_plans(plans, steps, warmup, torch, per_launch_steps):
+    """Time `steps` steps cycling over the buffer sets in `plans` (lists of launches,
+    all of the same kinds in the same order), with HIP events only at the two ends.
+    Then per-launch durations from events between consecutive launches over
+    `per_launch_steps` more steps.  Returns (ms per step, [(launch, avg ms, median ms)])."""
+    def step(i, events=None):
+        for j, l in enumerate(plans[i % len(plans)]):
+            if events is not None:
+                events[j].record()
+            l.fn()
+        if events is not None:
+            events[len(plans[0])].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    n = len(plans[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(per_launch_steps)]
+    for i in range(per_launch_steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    rows = []
+    for j, l in enumerate(plans[0]):
+        d = sorted(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(per_launch_steps))
+        rows.append((l, sum(d) / len(d), d[len(d) // 2]))
+    return ms_per_step, rows
+
+
+# The smaller workloads reported beside the layer step: each timed on its own, its
+# buffer sets rotated until their footprint exceeds 512 MB (twice the 256 MB of
+# L2 + MALL), so that no step finds its inputs in the caches from the previous one.
+CONFIGS = ["tiny_fprop", "qkv_fprop", "mlp_fprop", "mlp_down_bwd"]
+ROTATE_BYTES = 512 << 20
+
+
+def config_report(name, puro, torch, seed, steps, warmup):
+    import workloads
+    base = workloads.make(name, seed=seed, device="cuda")
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    plans, keep = [], []
+    launches, k = build_plan(name, base, puro, torch)
+    plans.append(launches)
+    keep.append((base, k))
+    per_set = torch.cuda.memory_allocated() - m0 + sum(t.numel() * t.element_size() for t in base.values())
+    sets = max(1, -(-ROTATE_BYTES // per_set) + (1 if ROTATE_BYTES % per_set == 0 else 0))
+    for _ in range(sets - 1):
+        t = {kk: v.clone() for kk, v in base.items()}
+        launches, k = build_plan(name, t, puro, torch)
+        plans.append(launches)
+        keep.append((t, k))
+    torch.cuda.synchronize()
+    ms, rows = time_plans(plans, steps, warmup, torch, steps)
+    flops = sum(l.flops for l in plans[0])
+    gemm_ms = sum(a for l, a, _ in rows if l.kind.startswith("gemm"))
+    q_ms = sum(a for l, a, _ in rows if l.kind == "quant")
+    q_bytes = sum(l.bytes for l in plans[0] if l.kind == "quant")
+    r = {
+        "workload": WORKLOAD_DESC[name],
+        "ms_per_step": round(ms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+        "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+        "gemm_pct_fp8_peak": round(100 * flops / (gemm_ms * 1e-3) / PEAK_FP8_FLOPS, 1),
+        "quant_gbps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+        "quant_pct_hbm_peak": round(100 * q_bytes / (q_ms * 1e-3) / PEAK_HBM_BPS, 1),
+        "buffer_sets": sets,
+        "footprint_mb": round(sets * per_set / 1e6),
+        "kernels": [{"name": l.name, "ms_avg": round(a, 4),
+                     **({"tflops": round(l.flops / (a * 1e-3) / 1e12, 1),
+                         "pct_fp8_peak": round(100 * l.flops / (a * 1e-3) / PEAK_FP8_FLOPS, 1)} if l.flops else
+                        {"gbps": round(l.bytes / (a * 1e-3) / 1e9, 1),
+                         "pct_hbm_peak": round(100 * l.bytes / (a * 1e-3) / PEAK_HBM_BPS, 1)})}
+                    for l, a, _ in rows],
+    }
+    if name == "tiny_fprop":
+        r["note"] = "launch-bound (0.07 GFLOP): a parity case, not a throughput target"
+    del plans, keep
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -486,7 +603,21 @@ def main():
     else:
         tensors = workloads.make(args.workload, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
     launches, keep = build_plan(args.workload, tensors, puro, torch)
+    # Workloads smaller than 512 MB (inputs, outputs, workspaces) rotate over as many
+    # copies of their buffers as it takes to exceed it, so that a step does not find
+    # its inputs in L2 or the 256 MB MALL from the step before.
+    per_set = torch.cuda.memory_allocated() - m0
+    if args.workload != "requant":            # the requantizer's step reads only the saved codes
+        per_set += sum(t.numel() * t.element_size() for t in tensors.values())
+    plans, sets_keep = [launches], [keep]
+    while len(plans) * per_set <= ROTATE_BYTES:
+        t = {k: v.clone() for k, v in tensors.items()}
+        extra, k = build_plan(args.workload, t, puro, torch)
+        plans.append(extra)
+        sets_keep.append((t, k))
+    torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -497,13 +628,17 @@ def main():
         else:
             cpu = cpu_baseline(tensors, args.workload, args.cpu_seconds)
 
+    counter = [0]
+
     def step(events=None):
-        for i, l in enumerate(launches):
+        plan = plans[counter[0] % len(plans)]
+        counter[0] += 1
+        for i, l in enumerate(plan):
             if events is not None:
                 events[i].record()
             l.fn()
         if events is not None:
-            events[len(launches)].record()
+            events[len(plan)].record()
 
     for _ in range(args.warmup):
         step()
@@ -596,6 +731,15 @@ def main():
     tr = load_traffic(dom_kind)
     roof["traffic"] = tr
 
+    configs = None
+    if args.workload == "layer" and not args.no_configs:
+        configs = {}
+        for name in CONFIGS:
+            configs[name] = config_report(name, puro, torch, args.seed, args.config_steps, args.config_steps)
+            print("config %s: %.4f ms per step" % (name, configs[name]["ms_per_step"]), file=sys.stderr, flush=True)
+    if cpu is not None:
+        cpu["cpu_model"] = cpu_model()
+
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -620,9 +764,12 @@ def main():
         "requant_gbps": (round(kinds["requant"]["bytes"] / (kinds["requant"]["ms"] * 1e-3) / 1e9, 1)
                          if "requant" in kinds else None),
         "wall_s_timed": round(wall, 3),
+        "buffer_sets": len(plans),
+        "footprint_mb": round(len(plans) * per_set / 1e6),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": rows,
+        "configs": configs,
     }
     print(json.dumps(out))
 
