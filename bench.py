@@ -6,7 +6,8 @@ One step = one pass of the whole path over one Qwen3-1.7B-shaped layer
 16384 tokens: for each of the four main linears (QKV 2048->4096, O
 2048->2048, gate_up 2048->12288, down 6144->2048)
   - dual 128x1 / 1x128 quantization of the input X (one read of X),
-  - dual transposed / plain 128x128 quantization of the weight W,
+  - dual transposed / plain 128x128 quantization of the weight W (the four
+    weights in one launch at the start of the step),
   - dual 128x1 / 1x128 quantization of the output gradient dY,
   - fprop  Y  = X W^T     (bf16 out),
   - dgrad  dX = dY W      (bf16 out),
@@ -168,6 +169,20 @@ def build_plan(workload, tensors, puro, torch):
                                bytes_=R * C * (2 + 1 + 4 / 16384)))
         return (q, s), None
 
+    def q_weights(ws, name):
+        """All of the layer's weights in one launch, dual (128x128 codes and their transpose)."""
+        descs, outs, total = [], [], 0
+        for w in ws:
+            R, C = w.shape
+            q, s = alloc((R, C), torch.uint8), alloc((cdiv(R, 128), cdiv(C, 128)), torch.float32)
+            qt, st = alloc((C, R), torch.uint8), alloc((cdiv(C, 128), cdiv(R, 128)), torch.float32)
+            descs.append((w.data_ptr(), R, C, q.data_ptr(), s.data_ptr(), qt.data_ptr(), st.data_ptr()))
+            outs.append(((q, s), (qt, st)))
+            total += R * C * (2 + 2 * (1 + 4 / 16384))
+        arr = [puro.PuroWeight(*d) for d in descs]
+        launches.append(Launch("quant", name, lambda: check(puro.puro_quant_weights(arr, stream), name), bytes_=total))
+        return outs
+
     def requant(saved, name):
         q, s = saved
         R, C = q.shape
@@ -238,30 +253,33 @@ def build_plan(workload, tensors, puro, torch):
 
     if workload in ("layer", "layer_accum"):
         from workloads import LINEARS
+        wq = dict(zip(LINEARS, q_weights([tensors["w_" + lin] for lin in LINEARS], "weights.quant_w")))
         for lin in LINEARS:
-            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            x, dy = tensors["x_" + lin], tensors["dy_" + lin]
             xrow, xt = q_act_dual(x, lin + ".quant_x")
-            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            wrow, wt = wq[lin]
             dyrow, dyt = q_act_dual(dy, lin + ".quant_dy")
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
             gemm(puro.WGRAD, dyt, xt, torch.float32, lin + ".wgrad", accumulate=workload == "layer_accum")
     elif workload == "layer_tm":
         from workloads import LINEARS
+        wq = dict(zip(LINEARS, q_weights([tensors["w_" + lin] for lin in LINEARS], "weights.quant_w")))
         for lin in LINEARS:
-            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            x, dy = tensors["x_" + lin], tensors["dy_" + lin]
             xrow, xc = q_act_tm(x, lin + ".quant_x")
-            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            wrow, wt = wq[lin]
             dyrow, dyc = q_act_tm(dy, lin + ".quant_dy")
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")
             gemm(3, dyc, xc, torch.float32, lin + ".wgrad")
     elif workload == "layer_fp8_saved":
         from workloads import LINEARS
+        wq = dict(zip(LINEARS, q_weights([tensors["w_" + lin] for lin in LINEARS], "weights.quant_w")))
         for lin in LINEARS:
-            x, w, dy = tensors["x_" + lin], tensors["w_" + lin], tensors["dy_" + lin]
+            x, dy = tensors["x_" + lin], tensors["dy_" + lin]
             xrow = q_act(x, lin + ".quant_x")
-            wrow, wt = q_w_dual(w, lin + ".quant_w")
+            wrow, wt = wq[lin]
             dyrow, dyt = q_act_dual(dy, lin + ".quant_dy")
             gemm(puro.FPROP, xrow, wrow, torch.bfloat16, lin + ".fprop")
             gemm(puro.DGRAD, dyrow, wt, torch.bfloat16, lin + ".dgrad")

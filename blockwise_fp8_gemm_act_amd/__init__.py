@@ -7,7 +7,7 @@ device memory and streams.  There is no fallback: if the library is missing,
 importing this package fails.
 
 The raw C calls keep their C names (``puro_quant_act_1x128``,
-``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_requant_act_t``,
+``puro_quant_w_128x128``, ``puro_quant_transpose``, ``puro_quant_weights``, ``puro_requant_act_t``,
 ``puro_gemm_fp8_blockwise``, ``puro_gemm_fp8_blockwise_noalloc``,
 ``puro_gemm_fp8_blockwise_accumulate``,
 ``puro_gemm_fp8_swiglu_quant``, ...) and take integer device pointers.  The
@@ -53,6 +53,15 @@ _lib.puro_quant_transpose.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P, _P, 
 _lib.puro_quant_transpose.restype = ctypes.c_int
 _lib.puro_quant_act_128x1.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P]
 _lib.puro_quant_act_128x1.restype = ctypes.c_int
+
+
+class PuroWeight(ctypes.Structure):
+    """puro_weight: one entry of puro_quant_weights."""
+    _fields_ = [("w", _P), ("rows", _I64), ("cols", _I64), ("q", _P), ("s", _P), ("qt", _P), ("st", _P)]
+
+
+_lib.puro_quant_weights.argtypes = [ctypes.c_int, ctypes.POINTER(PuroWeight), _P]
+_lib.puro_quant_weights.restype = ctypes.c_int
 _lib.puro_requant_act_t.argtypes = [_P, _P, _I64, _I64, _P, _P, _P]
 _lib.puro_swiglu_quant.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P]
 _lib.puro_swiglu_quant.restype = ctypes.c_int
@@ -109,6 +118,12 @@ def puro_quant_transpose(kind, x, rows, cols, qt, st, q_row, s_row, stream=None)
 
 def puro_quant_act_128x1(x, rows, cols, qc, sc, q_row, s_row, stream=None) -> int:
     return _lib.puro_quant_act_128x1(x, rows, cols, qc, sc, q_row, s_row, stream)
+
+
+def puro_quant_weights(weights, stream=None) -> int:
+    """weights: a sequence of PuroWeight (or of 7-tuples w, rows, cols, q, s, qt, st)."""
+    arr = (PuroWeight * max(len(weights), 1))(*[w if isinstance(w, PuroWeight) else PuroWeight(*w) for w in weights])
+    return _lib.puro_quant_weights(len(weights), arr, stream)
 
 
 def puro_requant_act_t(q, s, rows, cols, qt, st, stream=None) -> int:
@@ -284,6 +299,32 @@ def quant_transpose(kind: int, x: torch.Tensor, dual: bool = False, stream=None)
                                 q.data_ptr() if dual else None, s.data_ptr() if dual else None,
                                 _stream(stream)), "puro_quant_transpose")
     return (qt, st, q, s) if dual else (qt, st)
+
+
+@_on_stream
+def quant_weights(ws, row: bool = True, transposed: bool = True, stream=None):
+    """Several weights (2-D bf16 CUDA tensors, at most 8) quantized in 128x128 blocks by one
+    launch.  Returns, per weight, (q, s) and/or (qt, st) as quant_w_128x128 and
+    quant_transpose(T_WEIGHT) return them: a list of tuples (q, s, qt, st) with None
+    for the outputs not requested."""
+    if not (row or transposed):
+        raise ValueError("request row-wise and/or transposed outputs")
+    if len(ws) > 8:
+        raise ValueError("at most 8 weights per call")
+    outs, descs = [], []
+    for i, w in enumerate(ws):
+        _bf16_input(w, "ws[%d]" % i)
+        R, C = w.shape
+        dev = w.device
+        q = empty((R, C), dtype=torch.uint8, device=dev) if row else None
+        s = empty((_cdiv(R, TILE), _cdiv(C, TILE)), dtype=torch.float32, device=dev) if row else None
+        qt = empty((C, R), dtype=torch.uint8, device=dev) if transposed else None
+        st = empty((_cdiv(C, TILE), _cdiv(R, TILE)), dtype=torch.float32, device=dev) if transposed else None
+        outs.append((q, s, qt, st))
+        ptr = lambda t: t.data_ptr() if t is not None else None
+        descs.append(PuroWeight(w.data_ptr(), R, C, ptr(q), ptr(s), ptr(qt), ptr(st)))
+    _check(puro_quant_weights(descs, _stream(stream)), "puro_quant_weights")
+    return outs
 
 
 @_on_stream

@@ -161,6 +161,57 @@ puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t ro
   return launched(puro::run_quant_t_w(x, rows, cols, qt, st, q_row, s_row, (hipStream_t)stream));
 }
 
+puro_status puro_quant_weights(int count, const puro_weight *weights, puro_stream_t stream) {
+  constexpr int kMax = 8;
+  if (count < 0 || count > kMax) return PURO_ERR_SHAPE;
+  if (count == 0) return PURO_OK;
+  if (!weights) return PURO_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    const puro_weight &w = weights[i];
+    if (!shape_ok(w.rows, w.cols) || w.cols % 16 != 0 || (w.qt && w.rows % 16 != 0)) return PURO_ERR_SHAPE;
+  }
+  // entries with no elements write nothing: their pointers are not looked at
+  int first = -1;
+  for (int i = 0; i < count && first < 0; ++i)
+    if (weights[i].rows > 0 && weights[i].cols > 0) first = i;
+  if (first < 0) return PURO_OK;
+  const bool row = weights[first].q != nullptr, tr = weights[first].qt != nullptr;
+  for (int i = 0; i < count; ++i) {
+    const puro_weight &w = weights[i];
+    if (w.rows == 0 || w.cols == 0) continue;
+    if ((w.q == nullptr) != (w.s == nullptr) || (w.qt == nullptr) != (w.st == nullptr)) return PURO_ERR_NULL;
+    if ((w.q != nullptr) != row || (w.qt != nullptr) != tr || (!row && !tr)) return PURO_ERR_NULL;
+    if (!w.w) return PURO_ERR_NULL;
+  }
+  Range in[kMax], out[4 * kMax];
+  int nin = 0, nout = 0;
+  for (int i = 0; i < count; ++i) {
+    const puro_weight &w = weights[i];
+    if (w.rows == 0 || w.cols == 0) continue;
+    if (!aligned16(w.w) || (row && (!aligned16(w.q) || !aligned16(w.s))) ||
+        (tr && (!aligned16(w.qt) || !aligned16(w.st))))
+      return PURO_ERR_ALIGN;
+    const int64_t blocks = cdiv(w.rows, 128) * cdiv(w.cols, 128);
+    in[nin++] = rng(w.w, w.rows * w.cols * 2);
+    out[nout++] = rng(w.q, row ? w.rows * w.cols : 0);
+    out[nout++] = rng(w.s, row ? blocks * 4 : 0);
+    out[nout++] = rng(w.qt, tr ? w.rows * w.cols : 0);
+    out[nout++] = rng(w.st, tr ? blocks * 4 : 0);
+  }
+  if (any_alias(in, nin, out, nout)) return PURO_ERR_ALIAS;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) total += cdiv(weights[i].rows, 128) * cdiv(weights[i].cols, 128);
+  if (total > kMaxDim) return PURO_ERR_SHAPE;
+  if (puro_status d = check_device()) return d;
+  puro::WeightQuant wq[kMax];
+  int n = 0;
+  for (int i = 0; i < count; ++i)
+    if (weights[i].rows > 0 && weights[i].cols > 0)
+      wq[n++] = puro::WeightQuant{weights[i].w, weights[i].rows, weights[i].cols, weights[i].q, weights[i].s,
+                                  weights[i].qt, weights[i].st};
+  return launched(puro::run_quant_weights(n, wq, (hipStream_t)stream));
+}
+
 puro_status puro_quant_act_128x1(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *qc, float *sc,
                                  uint8_t *q_row, float *s_row, puro_stream_t stream) {
   if (!shape_ok(rows, cols) || cols % 16 != 0) return PURO_ERR_SHAPE;

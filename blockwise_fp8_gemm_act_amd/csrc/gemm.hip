@@ -92,6 +92,7 @@ struct GemmArgs {
   int spl;         // slices per split
   int tile0;       // this launch covers output tiles tile0 .. tile0 + ntiles - 1
   int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
+  int bn;          // output tile width: 256, or 192 / 128 for the row-scaled kernel
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -221,6 +222,65 @@ __device__ __forceinline__ void dma_slice8ab(const void *abase, const void *bbas
       : "memory", "scc");
 }
 
+// Copies of one interior slice for a tile narrower than 256 columns: the
+// wave's 4 row groups of A (lane offsets v0..v3, LDS at lda + 1024 j) and its
+// NGB row groups of B (lane offsets vb[j], LDS at ldb + 1024 j).
+template <int NGB>
+__device__ __forceinline__ void dma_slice_narrow(const void *abase, const void *bbase, uint32_t v0, uint32_t v1,
+                                                 uint32_t v2, uint32_t v3, const uint32_t (&vb)[NGB], uint32_t lda,
+                                                 uint32_t ldb) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %5\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %5\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, %5\n\t"
+      "s_add_u32 m0, m0, 0x400\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(abase), "s"(lda)
+      : "memory", "scc");
+  if constexpr (NGB == 3) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %4\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %3, %4\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "s"(bbase), "s"(ldb)
+        : "memory", "scc");
+  } else {
+    static_assert(NGB == 2, "3 or 2 row groups of B per wave");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\t"
+        "s_add_u32 m0, m0, 0x400\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(save)
+        : "v"(vb[0]), "v"(vb[1]), "s"(bbase), "s"(ldb)
+        : "memory", "scc");
+  }
+}
+
 // The 8 copies of one token-major slice for this wave: copy j brings tile rows
 // 16w + 4j .. 16w + 4j + 3 of A (at `lds` + 1024 j) and of B (32 KB further),
 // 256 bytes each.  The row step is folded into the eight 64-bit bases; the
@@ -286,7 +346,7 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = 
   const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
   const int tn = tile / g.tiles_m;
   t.m0 = tm * kBM;
-  t.n0 = tn * (glu ? kBK : kBN);
+  t.n0 = tn * (glu ? kBK : g.bn);
   t.kb_begin = t.split * g.spl;
   t.kb_end = min(g.nk, t.kb_begin + g.spl);
   // Items that run on one XCD at the same time (item = b + rG, workgroup b on
@@ -298,7 +358,7 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = 
   // SwiGLU kernel (whose column tiles differ).
   t.rot = (int)(((unsigned)(tm & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
   t.rows_a = min((int)g.M - t.m0, kBM);
-  t.rows_b = glu ? kBN : min((int)g.N - t.n0, kBN);
+  t.rows_b = glu ? kBN : min((int)g.N - t.n0, g.bn);
   return t;
 }
 
@@ -315,8 +375,16 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 // slices as one stream: the first slice of the next item is copied while the
 // last slice of the current one is computed, and the current item's output
 // leaves with direct global stores that drain while the next item computes.
-template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false, bool kKT = false>
+// kNB: n-blocks of 16 columns per wave, so the tile is 256 x BN with BN = 32 kNB
+// (8: 256; the row-scaled kernel also comes with 6 and 4, BN = 192 and 128, so
+// that more shapes fill the compute units in whole rounds without a split of K).
+template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false, bool kKT = false,
+          int kNB = 8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
+  static_assert(kNB == 8 || (kRowScaledB && !kKT && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
+  constexpr int BN = 32 * kNB;            // tile width
+  constexpr int WN = 16 * kNB;            // columns per wave
+  constexpr int NGB = kNB / 2;            // 8-row groups of B copied by each wave
   static_assert(!kAcc || (!kBf16Out && !kToWs), "accumulate mode stores fp32 directly");
   static_assert(!kGlu || (!kRowScaledB && kBf16Out && !kToWs && !kAcc), "the SwiGLU epilogue follows an fprop");
   static_assert(!kKT || (kRowScaledB && !kGlu), "token-major operands are the wgrad's");
@@ -366,6 +434,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const uint32_t voff1 = kKT ? kt_voff(1, g.M) : (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
   const uint32_t voff2 = kKT ? kt_voff(0, g.N) : (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
   const uint32_t voff3 = kKT ? kt_voff(1, g.N) : (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
+  // Narrow tiles: wave w copies B row groups NGB w + j (j < NGB); the chunk
+  // swizzle takes bit 1 of the row group (row bit 4), which is not j's own here.
+  auto dma_chunk_b = [&](int j) {
+    const int grp = NGB * w + j;
+    return ((lane & 7) ^ (((rig >> 1) & 1) | ((((rig >> 2) ^ (grp >> 1)) & 1) << 2))) * 16;
+  };
+  uint32_t vb[NGB];
+#pragma unroll
+  for (int j = 0; j < NGB; ++j) vb[j] = (uint32_t)((8 * j + rig) * K + dma_chunk_b(j));
 
   // Per-lane values that only edge tiles, the ragged last slice and the scale
   // copies need are recomputed from an opaque lane id at each call, so that
@@ -377,11 +454,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const uint32_t ls = lds_s0 + buf * 2 * kBM * 4;
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
-    const bool full = tl.rows_a == kBM && tl.rows_b == kBN;
+    const bool full = tl.rows_a == kBM && tl.rows_b == BN;
     if (full && (g.M & 3) == 0 && (!kRowScaledB || (g.N & 3) == 0) && (w == 0 || kRowScaledB)) {
       // 16-byte-aligned rows: lane l brings the scales of rows (columns) 4l .. 4l+3
       const float *src = w == 0 ? g.sa + (int64_t)kb * g.M + tl.m0 : g.sb + (int64_t)kb * g.N + tl.n0;
-      dma16_s(src, (uint32_t)ln * 16, ls + (w == 0 ? 0 : kBM * 4));
+      if (w == 0 || BN == kBM || ln < BN / 4) dma16_s(src, (uint32_t)ln * 16, ls + (w == 0 ? 0 : kBM * 4));
       return;
     }
     if (w == 0) {
@@ -391,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     } else if constexpr (kRowScaledB) {
       const float *src = g.sb + (int64_t)kb * g.N + tl.n0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, tl.rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
+      for (int j = 0; j < BN / 64; ++j) dma4_s(src, (uint32_t)min(ln + 64 * j, tl.rows_b - 1) * 4, ls + kBM * 4 + 256 * j);
     } else if constexpr (kGlu) {
       // lane 0 brings the scale of the tile's gate block, lane 1 that of its up block
       const float *src = g.sb + (int64_t)(tl.n0 / kBK) * g.nk + kb;
@@ -448,8 +525,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const uint8_t *a_tile = g.a + (int64_t)tl.m0 * g.K;
     const uint8_t *b_tile = g.b + (int64_t)tl.n0 * g.K;
-    if (tl.rows_a == kBM && tl.rows_b == kBN && !(ktail && kb == g.nk - 1)) {
-      if constexpr (kGlu) {
+    if (tl.rows_a == kBM && tl.rows_b == BN && !(ktail && kb == g.nk - 1)) {
+      if constexpr (kNB != 8) {
+        dma_slice_narrow<NGB>(a_tile + (int64_t)(w * 32) * g.K + kofs, b_tile + (int64_t)(w * 8 * NGB) * g.K + kofs,
+                              voff0, voff1, voff2, voff3, vb, la + w * 4096, la + kSliceBytes + w * (1024 * NGB));
+      } else if constexpr (kGlu) {
         // the wave's row groups 4w .. 4w+3 start at gate row n0 + 16w
         int ln = __lane_id();
         asm volatile("" : "+v"(ln));
@@ -475,10 +555,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         const int kc = dma_chunk(ln, j);
         const bool kin = kofs + kc < K;
         const uint8_t *pa = kin ? a_tile + kofs + (r < tl.rows_a ? (int64_t)r * K : 0) + kc : g_zero16;
-        const int64_t br = kGlu ? glu_brow(r) : (r < tl.rows_b ? (int64_t)r : 0);
-        const uint8_t *pb = kin ? b_tile + kofs + br * K + kc : g_zero16;
         dma16_v(pa, la + grp * 1024);
-        dma16_v(pb, lb + grp * 1024);
+        if constexpr (kNB == 8) {
+          const int64_t br = kGlu ? glu_brow(r) : (r < tl.rows_b ? (int64_t)r : 0);
+          const uint8_t *pb = kin ? b_tile + kofs + br * K + kc : g_zero16;
+          dma16_v(pb, lb + grp * 1024);
+        }
+      }
+      if constexpr (kNB != 8) {
+#pragma unroll
+        for (int j = 0; j < NGB; ++j) {
+          const int grp = NGB * w + j;
+          const int r = grp * 8 + rg;
+          const int kc = ((ln & 7) ^ (((rg >> 1) & 1) | ((((rg >> 2) ^ (grp >> 1)) & 1) << 2))) * 16;
+          const bool kin = kofs + kc < K;
+          const uint8_t *pb = kin ? b_tile + kofs + (r < tl.rows_b ? (int64_t)r * K : 0) + kc : g_zero16;
+          dma16_v(pb, lb + grp * 1024);
+        }
       }
     }
     issue_scales(tl, kb, buf);
@@ -505,11 +598,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   const uint32_t boff0 = (uint32_t)(cfr * kBK + ((2 * q) ^ swz_b(0)) * 16);
   const uint32_t boff1 = (uint32_t)(cfr * kBK + ((2 * q) ^ swz_b(1)) * 16);
 
-  v4f acc[4][8];
+  v4f acc[4][kNB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   auto frag = [](const uint8_t *row_base, uint32_t off) -> v8i {
     const v4i lo = *reinterpret_cast<const v4i *>(row_base + off);
@@ -542,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   };
   auto load_fragB = [&](const uint8_t *base, int nb) -> v8i {
     if constexpr (kKT) return frag_tr(base, wn * 128 + nb * 16);
-    return frag(base + (wn * 128 + 32 * (nb >> 1) + 4 * (nb & 1)) * kBK, (nb & 1) ? boff1 : boff0);
+    return frag(base + (wn * WN + 32 * (nb >> 1) + 4 * (nb & 1)) * kBK, (nb & 1) ? boff1 : boff0);
   };
   // first B-fragment column of n-block nb seen by lane (q, fr), relative to the wave's 128
   // (token-major tiles: the 16 fragment rows are 16 consecutive columns)
@@ -564,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const float *lsb = sscale[buf][1];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) sa[mb] = lsa[wm * 64 + mb * 16 + fr];
-    if constexpr (kRowScaledB) sbn0 = *reinterpret_cast<const v4f *>(&lsb[wn * 128 + colB(0)]);
+    if constexpr (kRowScaledB) sbn0 = *reinterpret_cast<const v4f *>(&lsb[wn * WN + colB(0)]);
     else if constexpr (kGlu) {
       sbk = lsb[0];
       sbu = lsb[1];
@@ -582,7 +675,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     const uint8_t *Bs = smem[buf][1];
     const float *lsb = sscale[buf][1];
     v4f P[4];
-    v4f sbv[8];                // row-scaled B: column scales of each n-block
+    v4f sbv[kNB];              // row-scaled B: column scales of each n-block
     sbv[0] = sbn0;
     float sc[4];               // block-scaled B: promotion factors sA * sB
     float scu[4];              // fused SwiGLU: those of the up n-blocks (odd nb)
@@ -598,9 +691,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     };
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       __builtin_amdgcn_sched_barrier(0);
-      if (nb == 7) {
+      if (nb == kNB - 1) {
         // Every wave holds its n-block 7 fragment (lgkmcnt) and has landed its
         // share of the next slice (vmcnt): past the barrier the next slice is
         // readable and nothing reads this slice's buffer any more.
@@ -608,15 +701,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kRowScaledB && nb + 1 < 8) sbv[nb + 1] = *reinterpret_cast<const v4f *>(&lsb[wn * 128 + colB(nb + 1)]);
-      if (nb + 1 < 8) bf[(nb + 1) & 1] = load_fragB(Bs, nb + 1);
-      if (nb == 7 && kPre) bf[0] = load_fragB(smem[buf ^ 1][1], 0);
+      if (kRowScaledB && nb + 1 < kNB) sbv[nb + 1] = *reinterpret_cast<const v4f *>(&lsb[wn * WN + colB(nb + 1)]);
+      if (nb + 1 < kNB) bf[(nb + 1) & 1] = load_fragB(Bs, nb + 1);
+      if (nb == kNB - 1 && kPre) bf[0] = load_fragB(smem[buf ^ 1][1], 0);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (nb > 0) promote(nb - 1, mb);
         P[mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
             bf[nb & 1], af[mb], (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-        if (nb == 7 && kPre) af[mb] = load_fragA(smem[buf ^ 1][0], mb);
+        if (nb == kNB - 1 && kPre) af[mb] = load_fragA(smem[buf ^ 1][0], mb);
         if (nb == 0 && !kRowScaledB) sc[mb] = sa[mb] * sbk;
         if (nb == 0 && kGlu) scu[mb] = sa[mb] * sbu;
       }
@@ -632,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
           if (!kRowScaledB) __builtin_amdgcn_sched_group_barrier(0x002, kGlu ? 2 : 1, 0);  // VALU
         }
-      } else if (nb < 7) {
+      } else if (nb < kNB - 1) {
         __builtin_amdgcn_sched_group_barrier(0x100, kF + kS, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -651,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) promote(7, mb);
+    for (int mb = 0; mb < 4; ++mb) promote(kNB - 1, mb);
     if constexpr (kPre) load_scales(buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -776,7 +869,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       glu_store(tl);
       return;
     }
-    const int64_t wbase = (int64_t)(tl.m0 + wm * 64) * g.N + tl.n0 + wn * 128;
+    const int64_t wbase = (int64_t)(tl.m0 + wm * 64) * g.N + tl.n0 + wn * WN;
     const int64_t loff = (int64_t)fr * g.N + 8 * q;
     typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
     auto pk = [](v4f v, int h) -> uint32_t {
@@ -787,18 +880,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       // split-K partial: the tile's own 256 x 256 fp32 block of the workspace,
       // [split][tile within the launch][row][column], written whole (rows and
       // columns past M / N hold finite values the reduction never reads)
-      float *o = g.ws + ((int64_t)tl.split * g.ntiles + tl.local) * (kBM * kBN) + (wm * 64) * kBN + wn * 128;
+      float *o = g.ws + ((int64_t)tl.split * g.ntiles + tl.local) * (kBM * BN) + (wm * 64) * BN + wn * WN;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        float *ob = o + (mb * 16 + fr) * kBN;
+        float *ob = o + (mb * 16 + fr) * BN;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<v4f *>(ob + colB(nb)) = acc[mb][nb];
+        for (int nb = 0; nb < kNB; ++nb) *reinterpret_cast<v4f *>(ob + colB(nb)) = acc[mb][nb];
       }
       return;
     }
     if constexpr (kKT) {
       // token-major tiles: lane (q, fr) holds columns 16nb + 4q .. +3 of n-block nb
-      if (tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0) {
+      if (tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0) {
         const int64_t lk = (int64_t)fr * g.N + 4 * q;
         if constexpr (kBf16Out && !kToWs) {
 #pragma unroll
@@ -829,13 +922,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     }
     if constexpr (kBf16Out && !kToWs) {
-      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 7) == 0;
+      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 7) == 0;
       if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
+          for (int pp = 0; pp < kNB / 2; ++pp) {
             const v4f a0 = acc[mb][2 * pp], a1 = acc[mb][2 * pp + 1];
             *reinterpret_cast<u32x4 *>(ob + loff + 32 * pp) = (u32x4){pk(a0, 0), pk(a0, 1), pk(a1, 0), pk(a1, 1)};
           }
@@ -847,8 +940,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           if (m >= g.M) continue;
           uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            const int n = tl.n0 + wn * 128 + colB(nb);
+          for (int nb = 0; nb < kNB; ++nb) {
+            const int n = tl.n0 + wn * WN + colB(nb);
             const uint32_t lo = pk(acc[mb][nb], 0), hi = pk(acc[mb][nb], 1);
             const uint16_t h[4] = {(uint16_t)(lo & 0xffffu), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xffffu),
                                    (uint16_t)(hi >> 16)};
@@ -861,13 +954,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     } else {
       float *o = reinterpret_cast<float *>(g.out) + wbase;
-      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == kBN && (g.N & 3) == 0;
+      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0;
       if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           float *ob = o + (int64_t)(mb * 16) * g.N;
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
+          for (int pp = 0; pp < kNB / 2; ++pp) {
             v4f *p0 = reinterpret_cast<v4f *>(ob + loff + 32 * pp);
             v4f *p1 = reinterpret_cast<v4f *>(ob + loff + 32 * pp + 4);
             if constexpr (kAcc) {
@@ -887,8 +980,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           if (m >= g.M) continue;
           float *ob = o + (int64_t)(mb * 16) * g.N;
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            const int n = tl.n0 + wn * 128 + colB(nb);
+          for (int nb = 0; nb < kNB; ++nb) {
+            const int n = tl.n0 + wn * WN + colB(nb);
             float *d = ob + (int64_t)fr * g.N + colB(nb);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -919,7 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = (v4f){0.f, 0.f, 0.f, 0.f};
     }
     for (int i = 1; i + 1 < cur.kb_end - cur.kb_begin; ++i) {
       slice(buf, cur, kb_at(cur, i + 1), std::true_type{}, std::true_type{}, std::false_type{});
@@ -977,28 +1070,30 @@ __device__ __forceinline__ void reduce_at(const float *ws, void *out, int64_t w,
   }
 }
 
-// Sum of the split-K partials of output tiles tile0 .. tile0 + ntiles - 1.
-// The workspace holds one 256 x 256 fp32 block per split and tile,
-// [split][tile - tile0][row][column].  With W elements per thread, index e
-// covers row (e / (256/W)) % 256, columns W * (e % (256/W)) .. +W-1 of tile
-// tile0 + e / (65536/W).  kVec needs N % 4 == 0 (a group of 4 columns is then
-// either wholly inside the output or wholly past its last column).
+// Sum of the split-K partials of output tiles tile0 .. tile0 + ntiles - 1
+// (tiles of 256 x bn).  The workspace holds one 256 x bn fp32 block per split
+// and tile, [split][tile - tile0][row][column].  With W elements per thread,
+// index e covers row (e / (bn/W)) % 256, columns W * (e % (bn/W)) .. +W-1 of
+// tile tile0 + e / (256 bn / W).  kVec needs N % 4 == 0 (a group of 4 columns
+// is then either wholly inside the output or wholly past its last column).
 template <bool kBf16Out, bool kAcc, bool kVec>
 __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *ws, void *out, int64_t M, int64_t N,
-                                                                  int tiles_m, int tile0, int ntiles, int splits) {
+                                                                  int tiles_m, int tile0, int ntiles, int splits,
+                                                                  int bn) {
   static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
   constexpr int W = kVec ? 4 : 1;
-  constexpr int kRowItems = kBN / W;
-  const int64_t stride = (int64_t)ntiles * kBM * kBN;
-  const int64_t total = (int64_t)ntiles * kBM * kRowItems;
+  const int row_items = bn / W;
+  const int64_t tile_elems = (int64_t)kBM * bn;
+  const int64_t stride = (int64_t)ntiles * tile_elems;
+  const int64_t total = (int64_t)ntiles * kBM * row_items;
   const int64_t gstride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gstride) {
-    const int t = (int)(e / (kBM * kRowItems));
+    const int t = (int)(e / (kBM * row_items));
     const int tile = tile0 + t;
-    const int r = (int)((e / kRowItems) % kBM), c = (int)(e % kRowItems) * W;
-    const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * kBN + c;
+    const int r = (int)((e / row_items) % kBM), c = (int)(e % row_items) * W;
+    const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * bn + c;
     if (m >= M || n >= N) continue;
-    reduce_at<kBf16Out, kAcc, kVec>(ws, out, (int64_t)t * (kBM * kBN) + r * kBN + c, m * N + n, stride, splits);
+    reduce_at<kBf16Out, kAcc, kVec>(ws, out, (int64_t)t * tile_elems + (int64_t)r * bn + c, m * N + n, stride, splits);
   }
 }
 
@@ -1020,58 +1115,101 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *p, int64_t n, u
 
 // ---------------------------------------------------------------- planning
 
-GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
-  GemmPlan p{};
-  p.nk = (int)((K + kBK - 1) / kBK);
-  p.tiles_m = (int)((M + kBM - 1) / kBM);
-  p.tiles_n = (int)((N + kBN - 1) / kBN);
+// Estimated time of one plan: rounds of 256 work items, each of its slices
+// plus about 2 slices of fixed cost (first copy, epilogue) at about 1.9 us per
+// 256 x 256 slice (a narrower tile's slice takes its share of that, times the
+// cost of its extra copies per flop), plus the workspace traffic (every split
+// writes an fp32 partial of its tiles and the reduction reads it back) at
+// about 4 TB/s.
+struct PlanCost {
+  double slice_us;     // one slice of one tile
+  double tile_bytes;   // fp32 partial of one tile
+};
+
+static PlanCost plan_cost(int bn) {
+  // per-slice times relative to a 256 x 256 tile's, measured on MI355X at the
+  // layer's weight-gradient shapes (a narrow tile copies more bytes per flop,
+  // so its slices cost more than its share of the work: 0.86 for 3/4 of it,
+  // 0.68 for half)
+  const double rel = bn == 256 ? 1.0 : bn == 192 ? 0.86 : 0.68;
+  return PlanCost{1.9e-6 * rel, 4.0 * kBM * bn};
+}
+
+static void plan_splits(GemmPlan &p, int64_t M, int64_t N, double &best) {
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  const PlanCost c = plan_cost(p.bn);
+  const double bw = 4.0e12;
   p.splits = 1;
   p.whole = 0;
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  best = 0.0;
   // Split the K loop when the output tiles fill the 256 compute units poorly
   // (a last round of tiles that leaves units idle, or fewer tiles than units).
-  // Estimated time of rounds of 256 work items, each of its slices plus about
-  // 2 slices of fixed cost (first copy, epilogue) at about 1.9 us per slice,
-  // plus the workspace traffic (every split writes an fp32 partial of its
-  // tiles and the reduction reads it back) at about 4 TB/s.  Two forms:
+  // Two forms:
   //  - every tile split s ways;
   //  - when the tiles fill w >= 1 whole rounds and leave r more, the first
   //    256w tiles computed whole by a first launch (direct stores, no
   //    workspace) and only the last r split s ways by a second one (about
   //    3 us more for the extra launch).
   // Splitting must win by 3%; at least 4 slices per split.
-  if (tiles > 0 && p.nk > 0) {
-    const double us = 1.9e-6, bw = 4.0e12, tile_bytes = 4.0 * kBM * kBN;
-    double best = 0.0;
-    for (int s = 1; s <= 8; ++s) {
-      const int spl = (p.nk + s - 1) / s;
-      if (s > 1 && (spl < 4 || (p.nk + spl - 1) / spl != s)) continue;
-      const double t = (double)((tiles * s + 255) / 256) * (spl + 2) * us +
-                       (s > 1 ? 2.0 * s * (double)M * (double)N * 4.0 / bw : 0.0);
-      if (s == 1 || t < best * 0.97) {
-        best = t;
-        p.splits = s;
-      }
+  for (int s = 1; s <= 8; ++s) {
+    const int spl = (p.nk + s - 1) / s;
+    if (s > 1 && (spl < 4 || (p.nk + spl - 1) / spl != s)) continue;
+    const double t = (double)((tiles * s + 255) / 256) * (spl + 2) * c.slice_us +
+                     (s > 1 ? 2.0 * s * (double)tiles * c.tile_bytes / bw : 0.0);
+    if (s == 1 || t < best * 0.97) {
+      best = t;
+      p.splits = s;
     }
-    const int64_t w = tiles / 256, r = tiles % 256;
-    for (int s = 2; w > 0 && r > 0 && s <= 8; ++s) {
-      const int spl = (p.nk + s - 1) / s;
-      if (spl < 4 || (p.nk + spl - 1) / spl != s) continue;
-      const double t = (double)w * (p.nk + 2) * us + (double)((r * s + 255) / 256) * (spl + 2) * us +
-                       2.0 * s * (double)r * tile_bytes / bw + 3.0e-6;
-      if (t < best * 0.97) {
-        best = t;
-        p.splits = s;
-        p.whole = (int)(w * 256);
+  }
+  const int64_t w = tiles / 256, r = tiles % 256;
+  for (int s = 2; w > 0 && r > 0 && s <= 8; ++s) {
+    const int spl = (p.nk + s - 1) / s;
+    if (spl < 4 || (p.nk + spl - 1) / spl != s) continue;
+    const double t = (double)w * (p.nk + 2) * c.slice_us + (double)((r * s + 255) / 256) * (spl + 2) * c.slice_us +
+                     2.0 * s * (double)r * c.tile_bytes / bw + 3.0e-6;
+    if (t < best * 0.97) {
+      best = t;
+      p.splits = s;
+      p.whole = (int)(w * 256);
+    }
+  }
+  (void)M;
+  (void)N;
+}
+
+GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{};
+  p.nk = (int)((K + kBK - 1) / kBK);
+  p.tiles_m = (int)((M + kBM - 1) / kBM);
+  p.bn = kBN;
+  p.tiles_n = (int)((N + kBN - 1) / kBN);
+  p.splits = 1;
+  p.whole = 0;
+  if (p.tiles_m > 0 && p.tiles_n > 0 && p.nk > 0) {
+    double best = 0.0;
+    plan_splits(p, M, N, best);
+    // The weight gradient (row-scaled B, operands K-contiguous) also has tiles
+    // 192 and 128 wide; a narrower tile must win by 3% too.
+    if (mode == 2) {
+      for (int bn : {192, 128}) {
+        GemmPlan q = p;
+        q.bn = bn;
+        q.tiles_n = (int)((N + bn - 1) / bn);
+        double t = 0.0;
+        plan_splits(q, M, N, t);
+        if (t < best * 0.97) {
+          best = t;
+          p = q;
+        }
       }
     }
   }
   p.spl = (p.nk + p.splits - 1) / p.splits;
   if (p.spl > 0) p.splits = (p.nk + p.spl - 1) / p.spl;
   if (p.splits == 1) p.whole = 0;
-  // one 256 x 256 fp32 block per split of each split tile
-  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)(tiles - p.whole) * kBM * kBN * sizeof(float) : 0;
-  (void)mode;
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+  // one 256 x bn fp32 block per split of each split tile
+  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)(tiles - p.whole) * kBM * p.bn * sizeof(float) : 0;
   return p;
 }
 
@@ -1090,17 +1228,18 @@ static int compute_units() {
   return n;
 }
 
-// One kernel of the family for a mode (RB: row-scaled B; KT: token-major operands).
-template <bool RB, bool KT>
+// One kernel of the family for a mode (RB: row-scaled B; KT: token-major
+// operands; NB: n-blocks per wave, the tile width over 32).
+template <bool RB, bool KT, int NB = 8>
 static void launch_mode(const dim3 &grid, hipStream_t stream, const GemmArgs &g, bool to_ws, bool acc, bool bf16) {
   if (to_ws)
-    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, true, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, true, false, false, KT, NB>), grid, dim3(kThreads), 0, stream, g);
   else if (acc)
-    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, true, false, KT>), grid, dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, true, false, KT, NB>), grid, dim3(kThreads), 0, stream, g);
   else if (bf16)
-    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, true, false, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, true, false, false, false, KT, NB>), grid, dim3(kThreads), 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, false, false, KT>), grid, dim3(kThreads), 0, stream, g);
+    hipLaunchKernelGGL((gemm_fp8_bw_kernel<RB, false, false, false, false, KT, NB>), grid, dim3(kThreads), 0, stream, g);
 }
 
 hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *b, const float *sb,
@@ -1119,7 +1258,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   GemmArgs g{};
   g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.out = out; g.ws = (float *)ws;
   g.M = M; g.N = N; g.K = K;
-  g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n;
+  g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n; g.bn = p.bn;
   const int tiles = p.tiles_m * p.tiles_n;
   const bool row_b = mode == 2 || mode == 3;
   // one persistent launch over tiles [tile0, tile0 + ntiles), each split s ways
@@ -1127,6 +1266,8 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (row_b && p.bn == 192) launch_mode<true, false, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (row_b && p.bn == 128) launch_mode<true, false, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
     else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
     return hipGetLastError();
@@ -1141,10 +1282,10 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   auto reduce = [&](auto bf16_c, auto acc_c, auto vec_c) {
     constexpr bool kB = decltype(bf16_c)::value, kA = decltype(acc_c)::value, kV = decltype(vec_c)::value;
     constexpr int W = kV ? 4 : 1;
-    const int64_t n = (int64_t)nt * kBM * kBN / W;
+    const int64_t n = (int64_t)nt * kBM * p.bn / W;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
     hipLaunchKernelGGL((splitk_reduce_tiles_kernel<kB, kA, kV>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
-                       p.tiles_m, p.whole, nt, p.splits);
+                       p.tiles_m, p.whole, nt, p.splits, p.bn);
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -1219,6 +1360,7 @@ hipError_t run_gemm_swiglu_quant(const uint8_t *a, const float *sa, const uint8_
   g.nk = (int)((K + kBK - 1) / kBK);
   g.tiles_m = (int)((M + kBM - 1) / kBM);
   g.tiles_n = (int)(I / kBK);
+  g.bn = kBN;
   g.splits = 1; g.spl = g.nk;
   g.tile0 = 0; g.ntiles = g.tiles_m * g.tiles_n;
   g.I = I; g.hq = hq; g.hs = hs;

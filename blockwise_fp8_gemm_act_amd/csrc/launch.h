@@ -20,6 +20,17 @@ hipError_t run_quant_act_128x1(const uint16_t *x, int64_t R, int64_t C, uint8_t 
                                float *s, hipStream_t stream);
 hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, float *st,
                          uint8_t *q, float *s, hipStream_t stream);
+// One launch over several weights (at most 8), each as run_quant_t_w / run_quant_w_128x128:
+// every entry has the same outputs (row-wise q, s and/or transposed qt, st).
+struct WeightQuant {
+  const uint16_t *w;
+  int64_t R, C;
+  uint8_t *q;
+  float *s;
+  uint8_t *qt;
+  float *st;
+};
+hipError_t run_quant_weights(int count, const WeightQuant *w, hipStream_t stream);
 hipError_t run_swiglu_quant(const uint16_t *gu, int64_t R, int64_t I, uint8_t *q, float *s, uint8_t *qt,
                             float *st, uint16_t *h, hipStream_t stream);
 hipError_t run_requant_act_t(const uint8_t *q, const float *s, int64_t R, int64_t C, uint8_t *qt,
@@ -31,6 +42,7 @@ struct GemmPlan {
   int splits;      // K-loop splits
   int spl;         // slices per split
   int whole;       // > 0: tiles 0 .. whole-1 run unsplit in a first launch, only the rest split
+  int bn;          // tile width: 256, or 192 / 128 (weight gradient)
   size_t ws_bytes; // fp32 split-K partials
 };
 

@@ -74,8 +74,9 @@ __device__ __forceinline__ void flush_transposed(const uint8_t *lds_t, uint8_t *
 //          input (gate = first C columns), computed in registers
 // kTRow: the 128x1 codes (kCol) leave in the input's own [R][C] layout
 // instead of transposed, for a wgrad that reads its operands token-major.
-template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false, bool kTRow = false>
-__global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
+// The work of one workgroup on block `bid` (row-major block index) of a.
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU, bool kTRow>
+__device__ __forceinline__ void quant_block(const QuantArgs &a, int64_t bid) {
   static_assert(!kTRow || (kCol && kWriteT), "the untransposed form is that of the 128x1 codes");
   __shared__ float lds_part[16 * kTile];                 // column partial maxima [rg][c]
   __shared__ float lds_rowamax[kTile];
@@ -86,7 +87,6 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
 
   const int t = threadIdx.x;
   const int cc = t & 15, rg = t >> 4;
-  const int64_t bid = blockIdx.x;
   const int64_t bi = bid / a.nj, bj = bid - bi * a.nj;
   const int64_t r0 = bi * kTile + rg * 8;
   const int64_t c0 = bj * kTile + cc * 8;
@@ -346,6 +346,32 @@ __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
   }
 }
 
+template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false, bool kTRow = false>
+__global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
+  quant_block<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU, kTRow>(a, blockIdx.x);
+}
+
+// Several weights quantized by one launch (128x128 blocks, row-major and/or
+// transposed outputs): a small weight alone fills only part of the chip for a
+// few microseconds, while the layer's weights together make thousands of
+// workgroups.  Workgroup b works on tensor i, block b - first[i], where
+// first[i] <= b < first[i + 1].
+constexpr int kMaxGroup = 8;
+struct QuantGroupArgs {
+  QuantArgs t[kMaxGroup];
+  int64_t first[kMaxGroup + 1];
+  int count;
+};
+
+template <bool kWriteRow, bool kWriteT>
+__global__ __launch_bounds__(256) void quant_weights_kernel(QuantGroupArgs g) {
+  const int64_t b = blockIdx.x;
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k) i += (k < g.count && b >= g.first[k]) ? 1 : 0;
+  quant_block<false, false, true, kWriteRow, kWriteT, false, false>(g.t[i], b - g.first[i]);
+}
+
 // Requantization of saved 1x128 activation codes into transposed 128x1 tiles:
 // each code is dequantized to fp32 with its row tile's scale (one IEEE
 // multiply, so the exact product rounded once), then quantized again with
@@ -569,6 +595,32 @@ hipError_t run_quant_t_w(const uint16_t *w, int64_t R, int64_t C, uint8_t *qt, f
   a.s = s;
   if (q) return launch_quant<false, false, true, true, true>(a, stream);
   return launch_quant<false, false, true, false, true>(a, stream);
+}
+
+hipError_t run_quant_weights(int count, const WeightQuant *w, hipStream_t stream) {
+  QuantGroupArgs g{};
+  g.count = count;
+  int64_t blocks = 0;
+  bool row = false, tr = false;
+  for (int i = 0; i < count; ++i) {
+    QuantArgs a = make_args(w[i].w, w[i].R, w[i].C);
+    a.q = w[i].q;
+    a.s = w[i].s;
+    a.qt = w[i].qt;
+    a.st = w[i].st;
+    row = a.q != nullptr;
+    tr = a.qt != nullptr;
+    g.t[i] = a;
+    g.first[i] = blocks;
+    blocks += a.ni * a.nj;
+  }
+  g.first[count] = blocks;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks);
+  if (row && tr) hipLaunchKernelGGL((quant_weights_kernel<true, true>), grid, dim3(256), 0, stream, g);
+  else if (tr) hipLaunchKernelGGL((quant_weights_kernel<false, true>), grid, dim3(256), 0, stream, g);
+  else hipLaunchKernelGGL((quant_weights_kernel<true, false>), grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t run_swiglu_quant(const uint16_t *gu, int64_t R, int64_t I, uint8_t *q, float *s, uint8_t *qt,

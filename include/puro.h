@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define PURO_ABI_VERSION 7
+#define PURO_ABI_VERSION 8
 
 /* Device scratch of puro_gemm_fp8_blockwise_noalloc, per GPU. */
 #define PURO_SCRATCH_BYTES (64ull << 20)
@@ -127,6 +127,35 @@ puro_status puro_quant_w_128x128(const uint16_t *w, int64_t rows, int64_t cols,
 puro_status puro_quant_transpose(puro_t_kind kind, const uint16_t *x, int64_t rows, int64_t cols,
                                  uint8_t *qt, float *st, uint8_t *q_row, float *s_row,
                                  puro_stream_t stream);
+
+/*
+ * puro_quant_weights -- several weights quantized in 128x128 blocks by one
+ * launch.  Each entry gets exactly what puro_quant_w_128x128 (q, s) and
+ * puro_quant_transpose(PURO_T_WEIGHT) (qt, st) write for it; a training step
+ * quantizes all of a layer's weights at once, and one launch over all of them
+ * keeps the chip busy where a small weight alone would not.
+ *   count    0 .. 8 entries (0 enqueues nothing)
+ *   weights  [count] descriptors (host memory, read during the call only):
+ *     w            bf16 [rows][cols] (input)
+ *     q, s         [rows][cols] codes, [ceil(rows/128)][ceil(cols/128)] scales,
+ *                  or both NULL
+ *     qt, st       [cols][rows] transposed codes, [ceil(cols/128)][ceil(rows/128)]
+ *                  scales, or both NULL
+ *   Every entry must request the same outputs (q, s and/or qt, st; at least
+ *   one pair).  cols must be a multiple of 16, and rows too when qt is
+ *   requested.  No output may overlap any input or output of any entry.  An
+ *   entry with rows or cols 0 writes nothing and its pointers are not used.
+ */
+typedef struct {
+    const uint16_t *w;
+    int64_t rows, cols;
+    uint8_t *q;
+    float *s;
+    uint8_t *qt;
+    float *st;
+} puro_weight;
+
+puro_status puro_quant_weights(int count, const puro_weight *weights, puro_stream_t stream);
 
 /*
  * puro_quant_act_128x1 -- the 128x1 tiles of puro_quant_transpose(PURO_T_ACT)

@@ -28,7 +28,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose", "puro_quant_act_128x1",
                             "puro_requant_act_t", "puro_swiglu_quant", "puro_gemm_workspace_bytes", "puro_gemm_fp8_blockwise",
-                            "puro_gemm_fp8_blockwise_noalloc",
+                            "puro_gemm_fp8_blockwise_noalloc", "puro_quant_weights",
                             "puro_gemm_fp8_blockwise_accumulate", "puro_gemm_fp8_swiglu_quant",
                             "puro_status_str", "puro_abi_version"])
 
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert puro.puro_abi_version() == 7
+    assert puro.puro_abi_version() == 8
     for s in range(11):
         assert puro.puro_status_str(s) and puro.puro_status_str(s) != "unknown status"
     assert puro.puro_status_str(99) == "unknown status"
@@ -257,7 +257,7 @@ def test_gemm_workspace_sizing():
     n = ws(2, 2048, 2048, 16384)
     assert n > 0 and n % tile == 0
     # the layer's split wgrads at 16384 tokens: qkv (128 tiles) in 2, o (64 tiles) in 4, gate_up
-    # (384 tiles: 256 whole, the other 128 in 2), down unsplit
+    # (384 tiles: 256 whole, the other 128 in 2), down unsplit (256 tiles 192 columns wide)
     assert ws(2, 4096, 2048, 16384) == 2 * 128 * tile
     assert ws(2, 2048, 2048, 16384) == 4 * 64 * tile
     assert ws(2, 12288, 2048, 16384) == 2 * 128 * tile
@@ -268,6 +268,10 @@ def test_gemm_workspace_sizing():
     assert ws(0, 1480, 10900, 1008) == 2 * 2 * tile
     # ragged edge tiles take a whole block too
     assert ws(2, 510, 511, 4096) % tile == 0
+    # weight-gradient shapes that narrower tiles fill in whole rounds need no workspace; a 128-column
+    # plan split over K takes 256 x 128 blocks
+    assert ws(2, 2048, 6144, 1024) == 0 and ws(2, 4096, 2048, 2048) == 0
+    assert ws(2, 2048, 2048, 8192) == 2 * 128 * 256 * 128 * 4
     # the fprop and dgrad shapes of the layer never split
     for M, N, K in [(16384, 4096, 2048), (16384, 2048, 2048), (16384, 12288, 2048), (16384, 2048, 6144),
                     (16384, 2048, 4096), (16384, 2048, 12288), (16384, 6144, 2048)]:
@@ -285,6 +289,38 @@ def test_gemm_workspace_errors():
     assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A4 + 16, need) == ALIAS
     if no_gpu():   # valid arguments: only safe to call with fake pointers when no device exists
         assert f(2, A0, A1, A2, A3, A4, 0, M, N, K, A5, need) == DEVICE
+
+
+def test_quant_weights_validation():
+    """The grouped weight quantizer checks every entry on the host before any launch."""
+    f = puro.puro_quant_weights
+    MB = 1 << 26
+    def wt(i, R=256, C=256, row=True, tr=True):
+        base = A0 + i * (1 << 32)
+        return (base, R, C, base + MB if row else None, base + 2 * MB if row else None,
+                base + 3 * MB if tr else None, base + 4 * MB if tr else None)
+    assert f([]) == OK
+    assert f([wt(i) for i in range(9)]) == SHAPE                     # at most 8
+    assert f([wt(0), wt(1, C=100)]) == SHAPE                         # cols not a multiple of 16
+    assert f([wt(0), wt(1, R=100)]) == SHAPE                         # transposed output needs rows % 16
+    assert f([wt(0), wt(1, R=100, tr=False)]) == NULL                # rows free without qt, but outputs differ
+    assert f([wt(0), wt(1, tr=False)]) == NULL                       # every entry the same outputs
+    assert f([wt(0, row=False, tr=False)]) == NULL                   # no output at all
+    bad = list(wt(1)); bad[4] = None
+    assert f([wt(0), tuple(bad)]) == NULL                            # q without s
+    bad = list(wt(1)); bad[0] = None
+    assert f([wt(0), tuple(bad)]) == NULL                            # no input
+    bad = list(wt(1)); bad[5] = bad[5] + 4
+    assert f([wt(0), tuple(bad)]) == ALIGN
+    bad = list(wt(1)); bad[3] = wt(0)[0]                             # an output over another entry's input
+    assert f([wt(0), tuple(bad)]) == ALIAS
+    bad = list(wt(1)); bad[5] = wt(0)[5]                             # two entries share an output
+    assert f([wt(0), tuple(bad)]) == ALIAS
+    assert f([(0, 0, 256, 0, 0, 0, 0), (0, 16, 0, 0, 0, 0, 0)]) == OK   # only empty entries: nothing to do
+    if no_gpu():
+        assert f([wt(0), wt(1, 2048, 6144), wt(2, 0, 512)]) == DEVICE
+        assert f([(0, 0, 256, 0, 0, 0, 0), wt(1, tr=False)]) == DEVICE     # empty entries are not compared
+        assert f([wt(i, tr=False) for i in range(8)]) == DEVICE
 
 
 def test_gemm_noalloc_validation():

@@ -11,6 +11,7 @@ import torch
 
 from helpers import (DGRAD, FPROP, WGRAD, bf16_bits_np, cdiv, check_gemm,
                      quantized_operands, to_np, TILE)
+from helpers import sample_positions as edge_samples
 from workloads import bits, make
 
 pytestmark = pytest.mark.gpu
@@ -101,7 +102,7 @@ def whole_then_split_check(orc, mode, a, sa, b, sb, out, dtype, what):
     check_gemm(orc, mode, a, sa, b, sb, out, what, ms, ns)
 
 
-@pytest.mark.parametrize("mode", [FPROP, WGRAD])
+@pytest.mark.parametrize("mode", [FPROP, DGRAD])
 @pytest.mark.parametrize("N", [10900, 10899])
 def test_whole_tiles_then_split_remainder(orc, mode, N):
     """258 output tiles (6 x 43) at 8 K slices: tiles 0-255 fill the compute units once and run whole in a
@@ -271,3 +272,35 @@ def test_helpers_reject_wrong_scale_layouts(orc):
     out = puro.gemm_fp8_blockwise(WGRAD, A, SA, B, SB, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert out.shape == (256, 256)
+
+
+@pytest.mark.parametrize("M,N,K,bn", [(2048, 6144, 1024, 192), (2000, 6100, 1040, 192), (4096, 2048, 2048, 128),
+                                      (4000, 2000, 2000, 128), (2048, 2048, 8192, 128), (2000, 1990, 8000, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_wgrad_narrow_tiles(orc, M, N, K, bn, dtype):
+    """Weight-gradient shapes for which the plan takes 192- or 128-column tiles (whole rounds of
+    256 work items): full and ragged edges, and a 128-column plan split over K (its partials summed by
+    the reduction in 256 x 128 blocks).  Every output checked; two calls give the same bits."""
+    a, sa, b, sb = quantized_operands(orc, WGRAD, M, N, K, seed=M + N + K + bn)
+    r1 = run_gpu(WGRAD, a, sa, b, sb, dtype)
+    # samples, the first and last rows, and every column of the last (ragged) tile column
+    ms, ns = edge_samples(M, N, 4096, M + N)
+    em, en = np.meshgrid(np.arange(0, M, 7), np.arange(N - (N % bn or bn), N), indexing="ij")
+    ms, ns = np.concatenate([ms, em.ravel()]), np.concatenate([ns, en.ravel()])
+    check_gemm(orc, WGRAD, a, sa, b, sb, r1, "wgrad %dx%dx%d" % (M, N, K), ms, ns)
+    r2 = run_gpu(WGRAD, a, sa, b, sb, dtype)
+    iv = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(r1.view(iv), r2.view(iv))
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 6144, 1024), (4096, 2048, 2048), (2048, 2048, 8192)])
+def test_wgrad_narrow_tiles_accumulate(orc, M, N, K):
+    """The narrow-tile plans in accumulate mode equal c + the plain result bit for bit."""
+    a, sa, b, sb = quantized_operands(orc, WGRAD, M, N, K, seed=M + N + 1)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    plain = to_np(run_gpu(WGRAD, a, sa, b, sb, torch.float32))
+    c = (np.random.default_rng(3).standard_normal((M, N)) * float(np.abs(plain).mean())).astype(np.float32)
+    out = dv(c)
+    puro.gemm_fp8_blockwise_accumulate(WGRAD, dv(a), dv(sa), dv(b), dv(sb), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(out), c + plain)

@@ -156,3 +156,28 @@ def test_workload_sizes(orc):
     check_t(orc, puro.T_ACT, t["dy_gate_up"], dual=True)
     check_w(orc, t["w_down"])
     check_t(orc, puro.T_WEIGHT, t["w_down"], dual=True)
+
+
+@pytest.mark.parametrize("outputs", ["both", "row", "transposed"])
+def test_quant_weights_grouped(orc, outputs):
+    """One launch over the layer's four weights plus ragged and empty ones: each entry's codes
+    and scales bit-exact against the oracle's 128x128 quantizer and its transpose."""
+    row, tr = outputs in ("both", "row"), outputs in ("both", "transposed")
+    t = make("layer", names={"w_" + lin for lin in LINEARS})
+    ws = [t["w_" + lin] for lin in LINEARS]
+    ws.append(special_input(272, 400, 5))            # ragged in both directions, special tiles
+    ws.append(outlier_input(0, 128, 6))               # empty
+    ws.append(outlier_input(144, 16, 7))
+    got = puro.quant_weights([w.cuda() for w in ws], row=row, transposed=tr)
+    torch.cuda.synchronize()
+    for i, (w, (q, s_, qt, st)) in enumerate(zip(ws, got)):
+        if w.numel() == 0:
+            continue
+        if row:
+            oq, os_ = orc.quant_w_128x128(bits(w))
+            assert_codes_equal(to_np(q), oq, "weight %d codes" % i)
+            assert_scales_equal(to_np(s_), os_, "weight %d scales" % i)
+        if tr:
+            oqt, ost = orc.quant_w_128x128_t(bits(w))
+            assert_codes_equal(to_np(qt), oqt, "weight %d transposed codes" % i)
+            assert_scales_equal(to_np(st), ost, "weight %d transposed scales" % i)
