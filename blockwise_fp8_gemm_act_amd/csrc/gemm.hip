@@ -91,9 +91,8 @@ struct GemmArgs {
   int splits;      // K-loop splits (1: no workspace)
   int spl;         // slices per split
   int tile0;       // this launch covers output tiles tile0 .. tile0 + ntiles - 1
-  int ntiles;      //   (tile t: see tile_rc)
+  int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
   int bn;          // output tile width: 256, or 192 / 128 for the row-scaled kernel
-  int n_major;     // tile order: 0 row tiles fastest, 1 column tiles fastest
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -338,38 +337,26 @@ struct Tile {
   int local;                 // tile index within this launch (tile - tile0): its block of the workspace
 };
 
-// Row and column tile of tile index t.  Consecutive tiles walk down M (they
-// share a B panel) or, in n-major order, along N (they share an A panel).
-__host__ __device__ __forceinline__ void tile_rc(int t, int tiles_m, int tiles_n, int n_major, int &tm, int &tn) {
-  if (n_major) {
-    tn = t % tiles_n;
-    tm = t / tiles_n;
-  } else {
-    tm = t % tiles_m;
-    tn = t / tiles_m;
-  }
-}
-
 // glu: the tile covers h columns n0 .. n0+127 (B rows: 128 gate + 128 up rows).
 __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = false) {
   Tile t;
   t.split = item / g.ntiles;
   t.local = item - t.split * g.ntiles;
-  int tm, tn;
-  tile_rc(g.tile0 + t.local, g.tiles_m, g.tiles_n, g.n_major, tm, tn);
+  const int tile = g.tile0 + t.local;
+  const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
+  const int tn = tile / g.tiles_m;
   t.m0 = tm * kBM;
   t.n0 = tn * (glu ? kBK : g.bn);
   t.kb_begin = t.split * g.spl;
   t.kb_end = min(g.nk, t.kb_begin + g.spl);
   // Items that run on one XCD at the same time (item = b + rG, workgroup b on
-  // XCD b % 8, G a multiple of 8) share item % 8, which is tm % 8 (tn % 8 in
-  // n-major order) when the tile count along the fast direction is a multiple
-  // of 8: they walk K in lockstep, sharing their A and B panels through that
-  // XCD's L2, and the 8 XCDs start 1/8 of the K range apart.  In the default
-  // order the rotation depends on the row tile alone, so an output element is
-  // summed in the same order by the plain fprop and by the fused SwiGLU kernel
-  // (whose column tiles differ).
-  t.rot = (int)(((unsigned)((g.n_major ? tn : tm) & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
+  // XCD b % 8, G a multiple of 8) share item % 8, which is tm % 8 when the
+  // row-tile count is a multiple of 8: they walk K in lockstep, sharing their
+  // A and B panels through that XCD's L2, and the 8 XCDs start 1/8 of the K
+  // range apart.  The order depends on the row tile alone, so an output
+  // element is summed in the same order by the plain fprop and by the fused
+  // SwiGLU kernel (whose column tiles differ).
+  t.rot = (int)(((unsigned)(tm & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
   t.rows_a = min((int)g.M - t.m0, kBM);
   t.rows_b = glu ? kBN : min((int)g.N - t.n0, g.bn);
   return t;
@@ -1091,8 +1078,8 @@ __device__ __forceinline__ void reduce_at(const float *ws, void *out, int64_t w,
 // is then either wholly inside the output or wholly past its last column).
 template <bool kBf16Out, bool kAcc, bool kVec>
 __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *ws, void *out, int64_t M, int64_t N,
-                                                                  int tiles_m, int tiles_n, int n_major, int tile0,
-                                                                  int ntiles, int splits, int bn) {
+                                                                  int tiles_m, int tile0, int ntiles, int splits,
+                                                                  int bn) {
   static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
   constexpr int W = kVec ? 4 : 1;
   const int row_items = bn / W;
@@ -1104,9 +1091,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *w
     const int t = (int)(e / (kBM * row_items));
     const int tile = tile0 + t;
     const int r = (int)((e / row_items) % kBM), c = (int)(e % row_items) * W;
-    int tm, tn;
-    tile_rc(tile, tiles_m, tiles_n, n_major, tm, tn);
-    const int64_t m = (int64_t)tm * kBM + r, n = (int64_t)tn * bn + c;
+    const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * bn + c;
     if (m >= M || n >= N) continue;
     reduce_at<kBf16Out, kAcc, kVec>(ws, out, (int64_t)t * tile_elems + (int64_t)r * bn + c, m * N + n, stride, splits);
   }
@@ -1221,11 +1206,6 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
   }
   p.spl = (p.nk + p.splits - 1) / p.splits;
   if (p.spl > 0) p.splits = (p.nk + p.spl - 1) / p.spl;
-  // A weight gradient with many more column tiles than row tiles (few output
-  // features, many input features) orders its tiles along N: the 32 items an
-  // XCD runs at once then cover tiles_n / 8 B panels and up to 8 A panels
-  // instead of one A panel and 32 B panels.
-  p.n_major = (mode == 2 || mode == 3) && p.tiles_n > p.tiles_m && p.tiles_n % 8 == 0 ? 1 : 0;
   if (p.splits == 1) p.whole = 0;
   const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
   // one 256 x bn fp32 block per split of each split tile
@@ -1278,7 +1258,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   GemmArgs g{};
   g.a = a; g.sa = sa; g.b = b; g.sb = sb; g.out = out; g.ws = (float *)ws;
   g.M = M; g.N = N; g.K = K;
-  g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n; g.bn = p.bn; g.n_major = p.n_major;
+  g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n; g.bn = p.bn;
   const int tiles = p.tiles_m * p.tiles_n;
   const bool row_b = mode == 2 || mode == 3;
   // one persistent launch over tiles [tile0, tile0 + ntiles), each split s ways
@@ -1305,7 +1285,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     const int64_t n = (int64_t)nt * kBM * p.bn / W;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
     hipLaunchKernelGGL((splitk_reduce_tiles_kernel<kB, kA, kV>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
-                       p.tiles_m, p.tiles_n, p.n_major, p.whole, nt, p.splits, p.bn);
+                       p.tiles_m, p.whole, nt, p.splits, p.bn);
   };
   using T = std::true_type;
   using F = std::false_type;

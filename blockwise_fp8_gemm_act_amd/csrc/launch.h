@@ -43,7 +43,6 @@ struct GemmPlan {
   int spl;         // slices per split
   int whole;       // > 0: tiles 0 .. whole-1 run unsplit in a first launch, only the rest split
   int bn;          // tile width: 256, or 192 / 128 (weight gradient)
-  int n_major;     // tile order: column tiles fastest (weight gradient with tiles_n > tiles_m)
   size_t ws_bytes; // fp32 split-K partials
 };
 
