@@ -61,6 +61,34 @@ def test_integer_valued_bit_exact(orc, mode, M, N, K):
     assert np.array_equal(out.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("mode", [FPROP, DGRAD])
+@pytest.mark.parametrize("M,N,K", [(4096, 4608, 256), (4096, 4608, 384), (8192, 2304, 1024), (2048, 2048, 128),
+                                   (4352, 4608, 2048)])
+def test_bf16_full_tiles_several_items_bit_exact(orc, mode, M, N, K):
+    """The bf16 output of full 256 x 256 tiles, with more tiles than workgroups (some
+    workgroups run 2 items, so an item's stores drain while the next item's first
+    slices run), K of 2 to 16 slices, and K = 128 (one slice per item).  Integer-valued codes with power-of-two scales
+    in [1/4, 4]: every partial sum is a multiple of 2^-4 below 2^20 (asserted through
+    the sum of |products|), exact in fp32 and fp64 in any order, so every bf16 element equals the oracle's rounding of the exact
+    value, which the product of the oracle's dequantized operands gives at this size."""
+    rng = np.random.default_rng(M + N + K + 10 * mode)
+    codes = np.array([orc.e4m3_encode(float(v)) for v in range(-8, 9)], dtype=np.uint8)
+    nk = cdiv(K, TILE)
+    a = rng.choice(codes, size=(M, K)).astype(np.uint8)
+    b = rng.choice(codes, size=(N, K)).astype(np.uint8)
+    sa = (np.float32(2.0) ** rng.integers(-2, 3, size=(nk, M))).astype(np.float32)
+    sb = (np.float32(2.0) ** rng.integers(-2, 3, size=(cdiv(N, TILE), nk))).astype(np.float32)
+    out = bf16_bits_np(run_gpu(mode, a, sa, b, sb, torch.bfloat16))
+    da, db = orc.dequant_a(a, sa), orc.dequant_b(mode, b, sb)
+    assert (np.abs(da) @ np.abs(db).T).max() < 2.0 ** 20       # bounds every partial sum
+    exact = da @ db.T
+    ms, ns = edge_samples(M, N, 512, M + N)
+    assert np.array_equal(exact[ms, ns], orc.gemm_at(mode, a, sa, b, sb, ms, ns))
+    ref = orc.f64_to_bf16_array(exact)
+    bad = np.argwhere(out != ref)
+    assert len(bad) == 0, "%d of %d elements differ, first at %s" % (len(bad), out.size, bad[:4].tolist())
+
+
 @pytest.mark.parametrize("mode", [FPROP, DGRAD, WGRAD])
 @pytest.mark.parametrize("M,N,K", [(200, 300, 144), (1, 17, 16), (257, 129, 400), (640, 384, 2048)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
