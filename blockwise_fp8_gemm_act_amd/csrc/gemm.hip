@@ -923,7 +923,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
     if constexpr (kBf16Out && !kToWs) {
       const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 7) == 0;
-      if (fast) {
+      if (fast && kNB % 4 == 0) {
+        // whole 128-byte row segments: lane pairs (fr, fr ^ 1) trade 16 bytes so that
+        // one store covers 64 columns of 8 rows (even rows, then odd rows)
+        const bool odd = fr & 1;
+        const int64_t cx = 8 * (q + 4 * (fr & 1));
+        const int64_t offx = (int64_t)(fr & ~1) * g.N + cx, offy = (int64_t)(fr | 1) * g.N + cx;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
+#pragma unroll
+          for (int t = 0; t < kNB / 4; ++t) {
+            const u32x4 d0 = (u32x4){pk(acc[mb][4 * t], 0), pk(acc[mb][4 * t], 1), pk(acc[mb][4 * t + 1], 0),
+                                     pk(acc[mb][4 * t + 1], 1)};
+            const u32x4 d1 = (u32x4){pk(acc[mb][4 * t + 2], 0), pk(acc[mb][4 * t + 2], 1), pk(acc[mb][4 * t + 3], 0),
+                                     pk(acc[mb][4 * t + 3], 1)};
+            const u32x4 e = odd ? d0 : d1;
+            u32x4 sw;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sw[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)e[j], 0xB1, 0xF, 0xF, false);
+            *reinterpret_cast<u32x4 *>(ob + offx + 64 * t) = odd ? sw : d0;
+            *reinterpret_cast<u32x4 *>(ob + offy + 64 * t) = odd ? d1 : sw;
+          }
+        }
+      } else if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
