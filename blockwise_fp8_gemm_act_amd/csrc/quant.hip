@@ -36,6 +36,7 @@ struct QuantArgs {
   uint8_t *qt;             // transposed codes [C][R] (or null)
   float *st;               // scales of the transposed codes
   uint16_t *h;             // SwiGLU output [R][C] in bf16 (or null)
+  int64_t band;            // launch order: workgroups walk down bands of `band` block rows (1: row-major)
 };
 
 // Transposed codes of one 128x128 block, staged in LDS, to global memory.
@@ -346,9 +347,19 @@ __device__ __forceinline__ void quant_block(const QuantArgs &a, int64_t bid) {
   }
 }
 
+// Workgroup b takes the blocks of a band of `band` block rows in column order
+// (block row fastest), the bands one after another; the last band may be
+// shorter.
 template <bool kRow, bool kCol, bool kBlock, bool kWriteRow, bool kWriteT, bool kSwiGLU = false, bool kTRow = false>
 __global__ __launch_bounds__(256) void quant_block_kernel(QuantArgs a) {
-  quant_block<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU, kTRow>(a, blockIdx.x);
+  int64_t bid = blockIdx.x;
+  if (a.band > 1) {
+    const int64_t per = a.band * a.nj;
+    const int64_t band = bid / per, local = bid - band * per;
+    const int64_t h = min(a.band, a.ni - band * a.band);
+    bid = (band * a.band + local % h) * a.nj + local / h;
+  }
+  quant_block<kRow, kCol, kBlock, kWriteRow, kWriteT, kSwiGLU, kTRow>(a, bid);
 }
 
 // Several weights quantized by one launch (128x128 blocks, row-major and/or
@@ -545,6 +556,11 @@ static QuantArgs make_args(const uint16_t *x, int64_t R, int64_t C) {
   a.ld = C;
   a.ni = (R + kTile - 1) / kTile;
   a.nj = (C + kTile - 1) / kTile;
+  // Inputs at least 64 blocks wide go in bands of 8 block rows: measured on
+  // the 16384 x 12288 gradient's dual quantizer, 0.172-0.173 ms against
+  // 0.187-0.188 ms row-major (column-major: 0.195 ms); narrower inputs gain
+  // nothing from it.
+  a.band = a.nj >= 64 ? 8 : 1;
   return a;
 }
 

@@ -70,7 +70,7 @@ def check_t(orc, kind, xb, dual):
         assert_scales_equal(to_np(res[3]), orow[1], "dual row scales")
 
 
-@pytest.mark.parametrize("R,C", [(256, 256), (37, 400), (130, 16), (1, 128), (64, 1040), (300, 2048)])
+@pytest.mark.parametrize("R,C", [(256, 256), (37, 400), (130, 16), (1, 128), (64, 1040), (300, 2048), (1040, 8320)])
 def test_act_1x128(orc, R, C):
     check_act(orc, outlier_input(R, C, R + C))
     check_act(orc, special_input(R, C, 3 * R + C))
@@ -83,15 +83,16 @@ def test_w_128x128(orc, R, C):
 
 
 @pytest.mark.parametrize("R,C", [(256, 384), (144, 80), (16, 16), (1024, 2064),
-                                 (16, 4096), (144, 4112), (400, 4096), (768, 6144)])
+                                 (16, 4096), (144, 4112), (400, 4096), (768, 6144), (1040, 8320), (2064, 8192)])
 @pytest.mark.parametrize("dual", [False, True])
 def test_transpose_act(orc, R, C, dual):
-    """Ragged rows and columns, from a single 16-row block to inputs 4096-6144 wide."""
+    """Ragged rows and columns, from a single 16-row block to inputs 4096-8320 wide (at least
+    64 blocks wide: launched in bands of 8 block rows, with a short last band)."""
     check_t(orc, puro.T_ACT, outlier_input(R, C, R + 2 * C), dual)
     check_t(orc, puro.T_ACT, special_input(R, C, R + 5), dual)
 
 
-@pytest.mark.parametrize("R,C", [(256, 384), (208, 144), (2048, 512)])
+@pytest.mark.parametrize("R,C", [(256, 384), (208, 144), (2048, 512), (400, 8320)])
 @pytest.mark.parametrize("dual", [False, True])
 def test_transpose_w(orc, R, C, dual):
     check_t(orc, puro.T_WEIGHT, random_bf16((R, C), R + C, std=0.02), dual)
