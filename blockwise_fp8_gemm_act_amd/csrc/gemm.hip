@@ -864,6 +864,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
   };
 
+  // fp32 pair (a0: columns c .. c+3, a1: c+4 .. c+7 of row fr) stored as whole 128-byte
+  // row segments: lane pairs (fr, fr ^ 1) trade 16 bytes through a DPP swap (moved as
+  // integer dwords), so that one store covers 32 columns of 8 rows (even rows, then odd
+  // rows) -- 8 whole cache lines.  rowx / rowy: the element offsets of rows fr & ~1 and
+  // fr | 1, plus column c + 4 (fr & 1).
+  auto store_f32_pair = [&](float *base, int64_t rowx, int64_t rowy, v4f a0, v4f a1) {
+    const bool odd = fr & 1;
+    const u32x4 e = __builtin_bit_cast(u32x4, odd ? a0 : a1);
+    u32x4 swu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) swu[j] = (uint32_t)__builtin_amdgcn_mov_dpp((int)e[j], 0xB1, 0xF, 0xF, false);
+    const v4f sw = __builtin_bit_cast(v4f, swu);
+    *reinterpret_cast<v4f *>(base + rowx) = odd ? sw : a0;
+    *reinterpret_cast<v4f *>(base + rowy) = odd ? a1 : sw;
+  };
+
   auto store_item = [&](const Tile &tl) {
     if constexpr (kGlu) {
       glu_store(tl);
@@ -881,6 +897,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       // [split][tile within the launch][row][column], written whole (rows and
       // columns past M / N hold finite values the reduction never reads)
       float *o = g.ws + ((int64_t)tl.split * g.ntiles + tl.local) * (kBM * BN) + (wm * 64) * BN + wn * WN;
+      if constexpr (!kKT) {
+        const int cx = 8 * q + 4 * (fr & 1);
+        const int rx = (fr & ~1) * BN + cx, ry = (fr | 1) * BN + cx;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int pp = 0; pp < kNB / 2; ++pp)
+            store_f32_pair(o + (mb * 16) * BN + 32 * pp, rx, ry, acc[mb][2 * pp], acc[mb][2 * pp + 1]);
+        return;
+      }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         float *ob = o + (mb * 16 + fr) * BN;
@@ -978,7 +1004,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     } else {
       float *o = reinterpret_cast<float *>(g.out) + wbase;
       const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0;
-      if (fast) {
+      if (fast && !kAcc) {
+        const int64_t cx = 8 * q + 4 * (fr & 1);
+        const int64_t rx = (int64_t)(fr & ~1) * g.N + cx, ry = (int64_t)(fr | 1) * g.N + cx;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int pp = 0; pp < kNB / 2; ++pp)
+            store_f32_pair(o + (int64_t)(mb * 16) * g.N + 32 * pp, rx, ry, acc[mb][2 * pp], acc[mb][2 * pp + 1]);
+      } else if (fast) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           float *ob = o + (int64_t)(mb * 16) * g.N;
