@@ -978,6 +978,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           }
         }
       } else if (fast) {
+        // 192-column tiles (an odd number of n-block pairs): half segments
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
@@ -1018,6 +1019,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           for (int pp = 0; pp < kNB / 2; ++pp)
             store_f32_pair(o + (int64_t)(mb * 16) * g.N + 32 * pp, rx, ry, acc[mb][2 * pp], acc[mb][2 * pp + 1]);
       } else if (fast) {
+        // accumulate mode: read, add, write back in the accumulators' own layout
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
           float *ob = o + (int64_t)(mb * 16) * g.N;
@@ -1025,14 +1027,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           for (int pp = 0; pp < kNB / 2; ++pp) {
             v4f *p0 = reinterpret_cast<v4f *>(ob + loff + 32 * pp);
             v4f *p1 = reinterpret_cast<v4f *>(ob + loff + 32 * pp + 4);
-            if constexpr (kAcc) {
-              const v4f o0 = *p0, o1 = *p1;
-              *p0 = o0 + acc[mb][2 * pp];
-              *p1 = o1 + acc[mb][2 * pp + 1];
-            } else {
-              *p0 = acc[mb][2 * pp];
-              *p1 = acc[mb][2 * pp + 1];
-            }
+            const v4f o0 = *p0, o1 = *p1;
+            *p0 = o0 + acc[mb][2 * pp];
+            *p1 = o1 + acc[mb][2 * pp + 1];
           }
         }
       } else {
