@@ -189,6 +189,24 @@ __device__ __forceinline__ void dma_slice8(const void *abase, const void *bbase,
       : "memory", "scc");
 }
 
+// One row group of A and the same row group of B: two of dma_slice8's eight
+// copies (M0 = lds for A, lds + 32 KB for B).
+__device__ __forceinline__ void dma_pair(const void *abase, const void *bbase, uint32_t v, uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(v), "s"(abase), "s"(bbase), "s"(lds)
+      : "memory", "scc");
+}
+
 // The same 8 copies with separate lane offsets for B (its rows do not follow
 // A's row pattern in the fused SwiGLU kernel).
 __device__ __forceinline__ void dma_slice8ab(const void *abase, const void *bbase, uint32_t a0, uint32_t a1,
@@ -384,9 +402,10 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 // (8: 256; the row-scaled kernel also comes with 6 and 4, BN = 192 and 128, so
 // that more shapes fill the compute units in whole rounds without a split of K).
 template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false, bool kKT = false,
-          int kNB = 8>
+          int kNB = 8, bool kSpread = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(kNB == 8 || (kRowScaledB && !kKT && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
+  static_assert(!kSpread || (kNB == 8 && !kKT && !kGlu && !kAcc), "spread copies: interior 256-wide tiles");
   constexpr int BN = 32 * kNB;            // tile width
   constexpr int WN = 16 * kNB;            // columns per wave
   constexpr int NGB = kNB / 2;            // 8-row groups of B copied by each wave
@@ -684,8 +703,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     sbv[0] = sbn0;
     float sc[4];               // block-scaled B: promotion factors sA * sB
     float scu[4];              // fused SwiGLU: those of the up n-blocks (odd nb)
-    // the buffer of the previous slice was released by the barrier inside it
-    if constexpr (kNext) issue_slice(nxt, kb_next, buf ^ 1);
+    // The buffer of the previous slice was released by the barrier inside it.
+    // kSpread (every tile interior, K a multiple of 128): the scales go out
+    // now and the operand copies one A/B row-group pair per n-block step over
+    // steps 0-3, so that no wave stalls behind a burst of eight copies.
+    if constexpr (kNext && !kSpread) issue_slice(nxt, kb_next, buf ^ 1);
+    if constexpr (kNext && kSpread) issue_scales(nxt, kb_next, buf ^ 1);
+    const uint8_t *spa = g.a + (int64_t)(nxt.m0 + w * 32) * g.K + kb_next * kBK;
+    const uint8_t *spb = g.b + (int64_t)(nxt.n0 + w * 32) * g.K + kb_next * kBK;
+    const uint32_t sla = lds0 + (buf ^ 1) * 2 * kSliceBytes + w * 4096;
     auto promote = [&](int pb, int mb) {
       const v4f prev = kFirst ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[mb][pb];
       if constexpr (kRowScaledB) {
@@ -704,6 +730,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         // readable and nothing reads this slice's buffer any more.
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kNext && kSpread && nb < 4) {
+        dma_pair(spa, spb, nb == 0 ? voff0 : nb == 1 ? voff1 : nb == 2 ? voff2 : voff3, sla + 1024 * nb);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kRowScaledB && nb + 1 < kNB) sbv[nb + 1] = *reinterpret_cast<const v4f *>(&lsb[wn * WN + colB(nb + 1)]);
@@ -953,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     }
     if constexpr (kBf16Out && !kToWs) {
-      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 7) == 0;
+      const bool fast = kSpread || (!kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 7) == 0);
       if (fast && kNB % 4 == 0) {
         // whole 128-byte row segments: lane pairs (fr, fr ^ 1) trade 16 bytes so that
         // one store covers 64 columns of 8 rows (even rows, then odd rows)
@@ -989,18 +1019,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           }
         }
       } else {
+        // edge tiles: lane values from an opaque lane id (none stays live across the K loop)
+        int ln = __lane_id();
+        asm volatile("" : "+v"(ln));
+        const int efr = ln & 15, eq = ln >> 4;
+        auto ecol = [&](int nb) { return kKT ? 16 * nb + 4 * eq : 32 * (nb >> 1) + 4 * (nb & 1) + 8 * eq; };
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+          const int m = tl.m0 + wm * 64 + mb * 16 + efr;
           if (m >= g.M) continue;
-          uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N;
+          uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16 + efr) * g.N;
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int n = tl.n0 + wn * WN + colB(nb);
+            const int n = tl.n0 + wn * WN + ecol(nb);
             const uint32_t lo = pk(acc[mb][nb], 0), hi = pk(acc[mb][nb], 1);
             const uint16_t h[4] = {(uint16_t)(lo & 0xffffu), (uint16_t)(lo >> 16), (uint16_t)(hi & 0xffffu),
                                    (uint16_t)(hi >> 16)};
-            uint16_t *d = ob + (int64_t)fr * g.N + colB(nb);
+            uint16_t *d = ob + ecol(nb);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (n + e < g.N) d[e] = h[e];
@@ -1009,7 +1044,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
       }
     } else {
       float *o = reinterpret_cast<float *>(g.out) + wbase;
-      const bool fast = !kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0;
+      const bool fast = kSpread || (!kKT && tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0);
       if (fast && !kAcc) {
         const int64_t cx = 8 * q + 4 * (fr & 1);
         const int64_t rx = (int64_t)(fr & ~1) * g.N + cx, ry = (int64_t)(fr | 1) * g.N + cx;
@@ -1033,15 +1068,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           }
         }
       } else {
+        int ln = __lane_id();
+        asm volatile("" : "+v"(ln));
+        const int efr = ln & 15, eq = ln >> 4;
+        auto ecol = [&](int nb) { return kKT ? 16 * nb + 4 * eq : 32 * (nb >> 1) + 4 * (nb & 1) + 8 * eq; };
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const int m = tl.m0 + wm * 64 + mb * 16 + fr;
+          const int m = tl.m0 + wm * 64 + mb * 16 + efr;
           if (m >= g.M) continue;
-          float *ob = o + (int64_t)(mb * 16) * g.N;
+          float *ob = o + (int64_t)(mb * 16 + efr) * g.N;
 #pragma unroll
           for (int nb = 0; nb < kNB; ++nb) {
-            const int n = tl.n0 + wn * WN + colB(nb);
-            float *d = ob + (int64_t)fr * g.N + colB(nb);
+            const int n = tl.n0 + wn * WN + ecol(nb);
+            float *d = ob + ecol(nb);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (n + e < g.N) d[e] = kAcc ? d[e] + acc[mb][nb][e] : acc[mb][nb][e];
@@ -1324,10 +1363,21 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   auto launch = [&](int tile0, int ntiles, int s, int spl, bool to_ws) {
     g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
+    // every tile interior and no ragged K slice: the spread-copy kernels
+    const bool spread = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0 && !accumulate;
     if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 192) launch_mode<true, false, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 128) launch_mode<true, false, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (row_b && spread && to_ws)
+      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, true, false, false, false, 8, true>), grid, dim3(kThreads), 0,
+                         stream, g);
+    else if (row_b && spread && !bf16_out)
+      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, false, 8, true>), grid, dim3(kThreads), 0,
+                         stream, g);
     else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (spread && bf16_out && !to_ws)
+      hipLaunchKernelGGL((gemm_fp8_bw_kernel<false, true, false, false, false, false, 8, true>), grid, dim3(kThreads), 0,
+                         stream, g);
     else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
     return hipGetLastError();
   };
