@@ -2,8 +2,10 @@
 
 The fixed-shape tests pick the edges they mean to hit; these draw shapes at random
 (fixed seeds, so every run checks the same ones) to reach combinations nobody picked:
-ragged M, N and K in every mode and output dtype, and quantizer inputs with ragged rows
-and columns, including inputs wide enough (64+ blocks) to take the banded launch order.
+ragged M, N and K in every mode and output dtype; whole-tile shapes (M and N multiples of
+256, K of 128), which run the kernels that spread each slice's copies over the first
+n-block steps and have no edge code; and quantizer inputs with ragged rows and columns,
+including inputs wide enough (64+ blocks) to take the banded launch order.
 """
 import numpy as np
 import pytest
@@ -23,6 +25,11 @@ def gemm_shapes(seed, n):
     return [(int(rng.integers(1, 700)), int(rng.integers(1, 700)), 16 * int(rng.integers(1, 100))) for _ in range(n)]
 
 
+def interior_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    return [(256 * int(rng.integers(1, 6)), 256 * int(rng.integers(1, 6)), 128 * int(rng.integers(1, 17))) for _ in range(n)]
+
+
 def quant_shapes(seed, n):
     """(R, C): C a multiple of 16; R a multiple of 16 too, as the transposed outputs need."""
     rng = np.random.default_rng(seed)
@@ -40,6 +47,19 @@ def test_gemm_random_shapes(orc, mode, M, N, K):
         out = puro.gemm_fp8_blockwise(mode, dv(a), dv(sa), dv(b), dv(sb), out_dtype=dtype)
         torch.cuda.synchronize()
         check_gemm(orc, mode, a, sa, b, sb, out, "random mode %d %dx%dx%d %s" % (mode, M, N, K, dtype))
+
+
+@pytest.mark.parametrize("mode", [FPROP, DGRAD, WGRAD])
+@pytest.mark.parametrize("M,N,K", interior_shapes(4096, 4) + [(512, 512, 8192)])
+def test_gemm_random_interior_shapes(orc, mode, M, N, K):
+    """Whole tiles only; (512, 512, 8192) gives the weight gradient a split-K plan, whose
+    partials then come from the spread-copy kernel too."""
+    a, sa, b, sb = quantized_operands(orc, mode, M, N, K, seed=17 * M + 5 * N + K)
+    dv = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    for dtype in (torch.float32, torch.bfloat16):
+        out = puro.gemm_fp8_blockwise(mode, dv(a), dv(sa), dv(b), dv(sb), out_dtype=dtype)
+        torch.cuda.synchronize()
+        check_gemm(orc, mode, a, sa, b, sb, out, "interior mode %d %dx%dx%d %s" % (mode, M, N, K, dtype))
 
 
 @pytest.mark.parametrize("R,C", quant_shapes(77, 6))
