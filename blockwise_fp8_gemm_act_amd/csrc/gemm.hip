@@ -19,7 +19,10 @@
 //    64 (M) x 128 (N): 4 x 8 blocks of 16x16, 128 fp32 accumulators per lane;
 //  - each 128-deep K slice of A and B (2 x 32 KB of e4m3) is copied global ->
 //    LDS by the DMA path (global_load_lds_dwordx4, no VGPR round trip) into
-//    one of two buffers while the other is consumed: 128 KB of the 160 KB LDS;
+//    one of two buffers while the other is consumed: 128 KB of the 160 KB LDS.
+//    When every tile of a launch is interior (kSpread), a slice's copies go
+//    out one A/B row-group pair per n-block step over the first four steps
+//    instead of in one burst, which stalls the issuing waves less;
 //  - one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 16x16 block of one
 //    slice, so its result is the slice partial P_kb; it is promoted at once:
 //    acc = fma(P, sA*sB, acc);
