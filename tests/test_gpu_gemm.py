@@ -379,3 +379,27 @@ def test_wgrad_narrow_tiles_accumulate(orc, M, N, K):
     puro.gemm_fp8_blockwise_accumulate(WGRAD, dv(a), dv(sa), dv(b), dv(sb), out)
     torch.cuda.synchronize()
     assert np.array_equal(to_np(out), c + plain)
+
+
+@pytest.mark.parametrize("mode", [FPROP, DGRAD])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (4096, 4352, 256)])
+def test_spread_copy_kernel_matches_edge_kernel(orc, mode, M, N, K):
+    """A whole-tile shape (M and N multiples of 256, K of 128, no split) runs the bf16 kernel
+    that spreads each slice's copies over the first n-block steps and has no edge code; the
+    same operands with 16 more rows of A, or of B, run the kernel with edge tiles.  Every
+    output's K sum runs in an order set by its row tile alone, so the outputs they share agree
+    bit for bit.  (4096, 4352, 256) gives each workgroup several items, so the next item's
+    first slice is copied during the current item's last one."""
+    a, sa, b, sb = quantized_operands(orc, mode, M + 16, N + 16, K, seed=M + 3 * N + 7 * K)
+    nb = N // TILE
+    inner = run_gpu(mode, np.ascontiguousarray(a[:M]), np.ascontiguousarray(sa[:, :M]),
+                    np.ascontiguousarray(b[:N]), np.ascontiguousarray(sb[:nb]), torch.bfloat16)
+    more_n = run_gpu(mode, np.ascontiguousarray(a[:M]), np.ascontiguousarray(sa[:, :M]), b, sb, torch.bfloat16)
+    more_m = run_gpu(mode, a, sa, np.ascontiguousarray(b[:N]), np.ascontiguousarray(sb[:nb]), torch.bfloat16)
+    want = out_np(inner)
+    assert np.array_equal(out_np(more_n)[:, :N], want), "16 more columns changed the shared outputs"
+    assert np.array_equal(out_np(more_m)[:M], want), "16 more rows changed the shared outputs"
+    # and the whole-tile result itself is within the rule (sampled at the larger shape)
+    ms, ns = (None, None) if M * N <= 1 << 20 else edge_samples(M, N, 20000, seed=M + N)
+    check_gemm(orc, mode, np.ascontiguousarray(a[:M]), np.ascontiguousarray(sa[:, :M]), np.ascontiguousarray(b[:N]),
+               np.ascontiguousarray(sb[:nb]), inner, "spread mode %d %dx%dx%d" % (mode, M, N, K), ms, ns)
