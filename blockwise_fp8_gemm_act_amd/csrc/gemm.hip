@@ -210,6 +210,25 @@ __device__ __forceinline__ void dma_pair(const void *abase, const void *bbase, u
       : "memory", "scc");
 }
 
+// One copy into A's half and one into B's (lds + 32 KB), with their own lane
+// offsets: a row-group pair of a token-major slice.
+__device__ __forceinline__ void dma_pair_ab(const void *abase, const void *bbase, uint32_t va, uint32_t vb,
+                                            uint32_t lds) {
+  uint32_t save;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %3\n\t"
+      "s_add_u32 m0, m0, 0x8000\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(save)
+      : "v"(va), "v"(vb), "s"(abase), "s"(bbase), "s"(lds)
+      : "memory", "scc");
+}
+
 // The same 8 copies with separate lane offsets for B (its rows do not follow
 // A's row pattern in the fused SwiGLU kernel).
 __device__ __forceinline__ void dma_slice8ab(const void *abase, const void *bbase, uint32_t a0, uint32_t a1,
@@ -408,7 +427,7 @@ template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool k
           int kNB = 8, bool kSpread = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(kNB == 8 || (kRowScaledB && !kKT && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
-  static_assert(!kSpread || (kNB == 8 && !kKT && !kGlu && !kAcc), "spread copies: interior 256-wide tiles");
+  static_assert(!kSpread || (kNB == 8 && !kGlu && !kAcc), "spread copies: interior 256-wide tiles");
   constexpr int BN = 32 * kNB;            // tile width
   constexpr int WN = 16 * kNB;            // columns per wave
   constexpr int NGB = kNB / 2;            // 8-row groups of B copied by each wave
@@ -712,8 +731,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     // steps 0-3, so that no wave stalls behind a burst of eight copies.
     if constexpr (kNext && !kSpread) issue_slice(nxt, kb_next, buf ^ 1);
     if constexpr (kNext && kSpread) issue_scales(nxt, kb_next, buf ^ 1);
-    const uint8_t *spa = g.a + (int64_t)(nxt.m0 + w * 32) * g.K + kb_next * kBK;
-    const uint8_t *spb = g.b + (int64_t)(nxt.n0 + w * 32) * g.K + kb_next * kBK;
+    // token-major slices: 16 token rows per wave, copy j the rows 4j .. 4j+3 of them
+    const uint8_t *spa = kKT ? g.a + ((int64_t)kb_next * kBK + 16 * w) * g.M + nxt.m0
+                             : g.a + (int64_t)(nxt.m0 + w * 32) * g.K + kb_next * kBK;
+    const uint8_t *spb = kKT ? g.b + ((int64_t)kb_next * kBK + 16 * w) * g.N + nxt.n0
+                             : g.b + (int64_t)(nxt.n0 + w * 32) * g.K + kb_next * kBK;
     const uint32_t sla = lds0 + (buf ^ 1) * 2 * kSliceBytes + w * 4096;
     auto promote = [&](int pb, int mb) {
       const v4f prev = kFirst ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[mb][pb];
@@ -736,7 +758,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kNext && kSpread && nb < 4) {
-        dma_pair(spa, spb, nb == 0 ? voff0 : nb == 1 ? voff1 : nb == 2 ? voff2 : voff3, sla + 1024 * nb);
+        if constexpr (kKT)
+          dma_pair_ab(spa + (int64_t)(4 * nb) * g.M, spb + (int64_t)(4 * nb) * g.N, (nb & 1) ? voff1 : voff0,
+                      (nb & 1) ? voff3 : voff2, sla + 1024 * nb);
+        else
+          dma_pair(spa, spb, nb == 0 ? voff0 : nb == 1 ? voff1 : nb == 2 ? voff2 : voff3, sla + 1024 * nb);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (kRowScaledB && nb + 1 < kNB) sbv[nb + 1] = *reinterpret_cast<const v4f *>(&lsb[wn * WN + colB(nb + 1)]);
@@ -955,7 +981,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     }
     if constexpr (kKT) {
       // token-major tiles: lane (q, fr) holds columns 16nb + 4q .. +3 of n-block nb
-      if (tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0) {
+      if (kSpread || (tl.rows_a == kBM && tl.rows_b == BN && (g.N & 3) == 0)) {
         const int64_t lk = (int64_t)fr * g.N + 4 * q;
         if constexpr (kBf16Out && !kToWs) {
 #pragma unroll
@@ -1368,7 +1394,13 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     // every tile interior and no ragged K slice: the spread-copy kernels
     const bool spread = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0 && !accumulate;
-    if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
+    if (mode == 3 && spread && to_ws)
+      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, true, false, false, true, 8, true>), grid, dim3(kThreads), 0,
+                         stream, g);
+    else if (mode == 3 && spread && !bf16_out)
+      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, true, 8, true>), grid, dim3(kThreads), 0,
+                         stream, g);
+    else if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 192) launch_mode<true, false, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 128) launch_mode<true, false, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && spread && to_ws)
