@@ -426,7 +426,7 @@ __device__ __forceinline__ int kb_at(const Tile &t, int i) {
 template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool kGlu = false, bool kKT = false,
           int kNB = 8, bool kSpread = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
-  static_assert(kNB == 8 || (kRowScaledB && !kKT && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
+  static_assert(kNB == 8 || (kRowScaledB && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
   static_assert(!kSpread || (kNB == 8 && !kGlu && !kAcc), "spread copies: interior 256-wide tiles");
   constexpr int BN = 32 * kNB;            // tile width
   constexpr int WN = 16 * kNB;            // columns per wave
@@ -470,16 +470,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   // c ^ kt_swz(k), kt_swz(k) = (k & 7) | ((k >> 5) & 1) << 3, so that the
   // transposing fragment reads below (rows 32q + 8s + r, r < 8) are free of
   // bank conflicts.  Lane l of copy j fills row 16w + 4j + l/16 at physical
-  // chunk l % 16; the offsets depend on j only through its parity.
-  auto kt_voff = [&](int j, int64_t ld) -> uint32_t {
+  // chunk l % 16; the offsets depend on j only through its parity.  A B tile
+  // narrower than 256 columns (nch chunks) keeps the 256-byte row: a lane
+  // whose logical chunk lies past the tile copies the tile's last chunk into
+  // a slot no fragment reads.
+  auto kt_voff = [&](int j, int64_t ld, int nch) -> uint32_t {
     const int kr = 4 * j + (lane >> 4);                       // row within the wave's 16 (< 16)
     const int sw = (kr & 7) | (((w >> 1) & 1) << 3);          // kt_swz(16w + kr)
-    return (uint32_t)((lane >> 4) * ld + (((lane & 15) ^ sw) << 4));
+    return (uint32_t)((lane >> 4) * ld + (min((lane & 15) ^ sw, nch - 1) << 4));
   };
-  const uint32_t voff0 = kKT ? kt_voff(0, g.M) : (uint32_t)(rig * K + dma_chunk(lane, 0));
-  const uint32_t voff1 = kKT ? kt_voff(1, g.M) : (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
-  const uint32_t voff2 = kKT ? kt_voff(0, g.N) : (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
-  const uint32_t voff3 = kKT ? kt_voff(1, g.N) : (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
+  const uint32_t voff0 = kKT ? kt_voff(0, g.M, 16) : (uint32_t)(rig * K + dma_chunk(lane, 0));
+  const uint32_t voff1 = kKT ? kt_voff(1, g.M, 16) : (uint32_t)((8 + rig) * K + dma_chunk(lane, 1));
+  const uint32_t voff2 = kKT ? kt_voff(0, g.N, BN / 16) : (uint32_t)((16 + rig) * K + dma_chunk(lane, 2));
+  const uint32_t voff3 = kKT ? kt_voff(1, g.N, BN / 16) : (uint32_t)((24 + rig) * K + dma_chunk(lane, 3));
   // Narrow tiles: wave w copies B row groups NGB w + j (j < NGB); the chunk
   // swizzle takes bit 1 of the row group (row bit 4), which is not j's own here.
   auto dma_chunk_b = [&](int j) {
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   auto issue_slice_kt = [&](const Tile &tl, int kb, int buf) {
     const uint32_t la = lds0 + buf * 2 * kSliceBytes;
     const int64_t k0 = (int64_t)kb * kBK + 16 * w;             // first token row of the wave's copies
-    if (tl.rows_a == kBM && tl.rows_b == kBN && !(ktail && kb == g.nk - 1)) {
+    if (tl.rows_a == kBM && tl.rows_b == BN && !(ktail && kb == g.nk - 1)) {
       const uint8_t *pa = g.a + k0 * g.M + tl.m0;
       const uint8_t *pb = g.b + k0 * g.N + tl.n0;
       dma_slice8kt(pa, pa + 4 * g.M, pa + 8 * g.M, pa + 12 * g.M, pb, pb + 4 * g.N, pb + 8 * g.N, pb + 12 * g.N,
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     return frag(base + (wm * 64 + mb * 16) * kBK, (mb & 1) ? aoff1 : aoff0);
   };
   auto load_fragB = [&](const uint8_t *base, int nb) -> v8i {
-    if constexpr (kKT) return frag_tr(base, wn * 128 + nb * 16);
+    if constexpr (kKT) return frag_tr(base, wn * WN + nb * 16);
     return frag(base + (wn * WN + 32 * (nb >> 1) + 4 * (nb & 1)) * kBK, (nb & 1) ? boff1 : boff0);
   };
   // first B-fragment column of n-block nb seen by lane (q, fr), relative to the wave's 128
@@ -988,7 +991,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           for (int mb = 0; mb < 4; ++mb) {
             uint16_t *ob = reinterpret_cast<uint16_t *>(g.out) + wbase + (int64_t)(mb * 16) * g.N + lk;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
+            for (int nb = 0; nb < kNB; ++nb)
               *reinterpret_cast<u32x2 *>(ob + 16 * nb) = (u32x2){pk(acc[mb][nb], 0), pk(acc[mb][nb], 1)};
           }
         } else {
@@ -997,7 +1000,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
           for (int mb = 0; mb < 4; ++mb) {
             float *ob = o + (int64_t)(mb * 16) * g.N + lk;
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) {
+            for (int nb = 0; nb < kNB; ++nb) {
               v4f *p0 = reinterpret_cast<v4f *>(ob + 16 * nb);
               if constexpr (kAcc) {
                 const v4f o0 = *p0;
@@ -1315,9 +1318,9 @@ GemmPlan plan_gemm(int mode, int64_t M, int64_t N, int64_t K) {
   if (p.tiles_m > 0 && p.tiles_n > 0 && p.nk > 0) {
     double best = 0.0;
     plan_splits(p, M, N, best);
-    // The weight gradient (row-scaled B, operands K-contiguous) also has tiles
-    // 192 and 128 wide; a narrower tile must win by 3% too.
-    if (mode == 2) {
+    // The weight gradient (row-scaled B, in both operand layouts) also has
+    // tiles 192 and 128 wide; a narrower tile must win by 3% too.
+    if (mode == 2 || mode == 3) {
       for (int bn : {192, 128}) {
         GemmPlan q = p;
         q.bn = bn;
@@ -1400,6 +1403,8 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     else if (mode == 3 && spread && !bf16_out)
       hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, true, 8, true>), grid, dim3(kThreads), 0,
                          stream, g);
+    else if (mode == 3 && p.bn == 192) launch_mode<true, true, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
+    else if (mode == 3 && p.bn == 128) launch_mode<true, true, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 192) launch_mode<true, false, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 128) launch_mode<true, false, 4>(grid, stream, g, to_ws, accumulate, bf16_out);

@@ -80,9 +80,11 @@ def test_integer_valued_bit_exact(orc, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 2048), (400, 272, 1040), (2048, 2048, 16384), (4096, 2048, 16384),
-                                   (2048, 6144, 8192), (16, 16, 16)])
+                                   (2048, 6144, 8192), (16, 16, 16), (2048, 6144, 1024), (2000, 6096, 1040),
+                                   (4096, 2048, 2048), (2000, 1984, 8000)])
 def test_equals_wgrad_on_transposed_operands(M, N, K):
-    """Same products, same promotion order: the bits of PURO_WGRAD on a^T, b^T."""
+    """Same products, same promotion order: the bits of PURO_WGRAD on a^T, b^T.  The last four
+    shapes plan 192- or 128-column tiles (whole and ragged), which both layouts then use."""
     a, sa, b, sb = operands(M, N, K, M + 7 * N + K)
     for dtype in (torch.float32, torch.bfloat16):
         got = run(WGRAD_TM, a, sa, b, sb, dtype)
