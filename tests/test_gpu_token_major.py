@@ -129,8 +129,9 @@ def test_workload_size_sampled(orc):
     check_gemm_values(to_np(out)[ms, ns], ref, na[ms], nb[ns], False, orc, "gate_up wgrad token-major")
 
 
-def test_accumulate_equals_c_plus_plain():
-    M, N, K = 2048, 2048, 16384                # split-K plan
+@pytest.mark.parametrize("M,N,K", [(2048, 2048, 16384), (2048, 6144, 1024), (4096, 2048, 2048)])
+def test_accumulate_equals_c_plus_plain(M, N, K):
+    """Split-K plan (256 columns), then unsplit 192- and 128-column plans."""
     a, sa, b, sb = operands(M, N, K, 77)
     plain = run(WGRAD_TM, a, sa, b, sb)
     c = torch.from_numpy(np.random.default_rng(1).standard_normal((M, N)).astype(np.float32)).cuda()
