@@ -124,3 +124,18 @@ def test_b_fragments_read_their_rows_without_bank_conflicts(nblocks):
                 want = wn * 16 * nblocks + 32 * (nb >> 1) + 4 * (nb & 1) + 8 * (fr >> 2) + (fr & 3)
                 assert reads[0][1] == want
             check_reads(frags)
+
+
+def test_plain_bank_mapping_would_conflict():
+    """The swizzle is fitted to gfx950's mapping: under a plain 64-bank mapping
+    (dword d -> d mod 64) the same A reads would conflict."""
+    frags = frag_a(0, 0)
+    worst = 0
+    for half in range(2):
+        for q in range(4):
+            banks = []
+            for fr in range(16):
+                addr = frags[(q, fr)][half][0]
+                banks += [((addr + 4 * i) // 4) % 64 for i in range(4)]
+            worst = max(worst, 64 - len(set(banks)))
+    assert worst > 0
