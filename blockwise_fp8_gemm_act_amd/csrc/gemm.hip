@@ -427,7 +427,7 @@ template <bool kRowScaledB, bool kBf16Out, bool kToWs, bool kAcc = false, bool k
           int kNB = 8, bool kSpread = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
   static_assert(kNB == 8 || (kRowScaledB && (kNB == 6 || kNB == 4)), "narrow tiles: row-scaled kernel only");
-  static_assert(!kSpread || (kNB == 8 && !kGlu && !kAcc), "spread copies: interior 256-wide tiles");
+  static_assert(!kSpread || (kNB == 8 && !kGlu), "spread copies: interior 256-wide tiles");
   constexpr int BN = 32 * kNB;            // tile width
   constexpr int WN = 16 * kNB;            // columns per wave
   constexpr int NGB = kNB / 2;            // 8-row groups of B copied by each wave
@@ -1396,26 +1396,30 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     // every tile interior and no ragged K slice: the spread-copy kernels
-    const bool spread = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0 && !accumulate;
-    if (mode == 3 && spread && to_ws)
-      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, true, false, false, true, 8, true>), grid, dim3(kThreads), 0,
-                         stream, g);
-    else if (mode == 3 && spread && !bf16_out)
-      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, true, 8, true>), grid, dim3(kThreads), 0,
-                         stream, g);
+    const bool interior = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0;
+    auto spread_rb = [&](auto kt_c) {                // row-scaled B: partials, accumulate or plain fp32
+      constexpr bool KT = decltype(kt_c)::value;
+      if (to_ws)
+        hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, true, false, false, KT, 8, true>), grid, dim3(kThreads), 0,
+                           stream, g);
+      else if (accumulate)
+        hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, true, false, KT, 8, true>), grid, dim3(kThreads), 0,
+                           stream, g);
+      else
+        hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, KT, 8, true>), grid, dim3(kThreads), 0,
+                           stream, g);
+    };
+    if (row_b && interior && (to_ws || !bf16_out)) {
+      if (mode == 3) spread_rb(std::true_type{});
+      else spread_rb(std::false_type{});
+    }
     else if (mode == 3 && p.bn == 192) launch_mode<true, true, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (mode == 3 && p.bn == 128) launch_mode<true, true, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (mode == 3) launch_mode<true, true>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 192) launch_mode<true, false, 6>(grid, stream, g, to_ws, accumulate, bf16_out);
     else if (row_b && p.bn == 128) launch_mode<true, false, 4>(grid, stream, g, to_ws, accumulate, bf16_out);
-    else if (row_b && spread && to_ws)
-      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, true, false, false, false, 8, true>), grid, dim3(kThreads), 0,
-                         stream, g);
-    else if (row_b && spread && !bf16_out)
-      hipLaunchKernelGGL((gemm_fp8_bw_kernel<true, false, false, false, false, false, 8, true>), grid, dim3(kThreads), 0,
-                         stream, g);
     else if (row_b) launch_mode<true, false>(grid, stream, g, to_ws, accumulate, bf16_out);
-    else if (spread && bf16_out && !to_ws)
+    else if (!row_b && interior && bf16_out && !to_ws && !accumulate)
       hipLaunchKernelGGL((gemm_fp8_bw_kernel<false, true, false, false, false, false, 8, true>), grid, dim3(kThreads), 0,
                          stream, g);
     else launch_mode<false, false>(grid, stream, g, to_ws, accumulate, bf16_out);
