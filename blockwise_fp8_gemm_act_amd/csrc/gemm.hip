@@ -101,6 +101,7 @@ struct GemmArgs {
   int tile0;       // this launch covers output tiles tile0 .. tile0 + ntiles - 1
   int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
   int bn;          // output tile width: 256, or 192 / 128 for the row-scaled kernel
+  int blocked;     // items in XCD blocks of 4 x 8 tiles (tile_of); set by the host
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -385,23 +386,44 @@ struct Tile {
 // glu: the tile covers h columns n0 .. n0+127 (B rows: 128 gate + 128 up rows).
 __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = false) {
   Tile t;
-  t.split = item / g.ntiles;
-  t.local = item - t.split * g.ntiles;
-  const int tile = g.tile0 + t.local;
-  const int tm = tile % g.tiles_m;       // consecutive items walk down M: they share B
-  const int tn = tile / g.tiles_m;
+  int tm, tn, xk;
+  if (g.blocked) {
+    // Blocked order (weight gradients whose whole tile grid, times the splits,
+    // fills rounds of 256 items; tiles_m % 4 == 0, tiles_n % 8 == 0).  Item
+    // 256r + 8w + x belongs to block 8r + x and is tile (w % 4, w / 4) of it:
+    // the 32 items that workgroups b = x (mod 8) run together on one XCD are
+    // one split of a 4 x 8 group of tiles, sharing 4 A and 8 B panels (12
+    // panels for 32 items, against 33 or more in the row-tile walk below when
+    // the row tiles are few).  Blocks run split-major, then along M, then N.
+    const int x = item & 7, w = (item >> 3) & 31, blk = ((item >> 8) << 3) | x;
+    const int bpm = g.tiles_m >> 2, bps = bpm * (g.tiles_n >> 3);
+    t.split = blk / bps;
+    const int bb = blk - t.split * bps;
+    tm = (bb % bpm) * 4 + (w & 3);
+    tn = (bb / bpm) * 8 + (w >> 2);
+    t.local = tn * g.tiles_m + tm;       // the launch covers every tile (tile0 = 0)
+    xk = x;
+  } else {
+    t.split = item / g.ntiles;
+    t.local = item - t.split * g.ntiles;
+    const int tile = g.tile0 + t.local;
+    tm = tile % g.tiles_m;               // consecutive items walk down M: they share B
+    tn = tile / g.tiles_m;
+    xk = tm & 7;
+  }
   t.m0 = tm * kBM;
   t.n0 = tn * (glu ? kBK : g.bn);
   t.kb_begin = t.split * g.spl;
   t.kb_end = min(g.nk, t.kb_begin + g.spl);
   // Items that run on one XCD at the same time (item = b + rG, workgroup b on
   // XCD b % 8, G a multiple of 8) share item % 8, which is tm % 8 when the
-  // row-tile count is a multiple of 8: they walk K in lockstep, sharing their
-  // A and B panels through that XCD's L2, and the 8 XCDs start 1/8 of the K
-  // range apart.  The order depends on the row tile alone, so an output
+  // row-tile count is a multiple of 8 (and the block's x in the blocked
+  // order): they walk K in lockstep, sharing their A and B panels through
+  // that XCD's L2, and the 8 XCDs start 1/8 of the K range apart.  In the
+  // row-tile walk the order depends on the row tile alone, so an output
   // element is summed in the same order by the plain fprop and by the fused
   // SwiGLU kernel (whose column tiles differ).
-  t.rot = (int)(((unsigned)(tm & 7) * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
+  t.rot = (int)(((unsigned)xk * (unsigned)(t.kb_end - t.kb_begin)) / 8u);
   t.rows_a = min((int)g.M - t.m0, kBM);
   t.rows_b = glu ? kBN : min((int)g.N - t.n0, g.bn);
   return t;
@@ -1394,6 +1416,11 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   // one persistent launch over tiles [tile0, tile0 + ntiles), each split s ways
   auto launch = [&](int tile0, int ntiles, int s, int spl, bool to_ws) {
     g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
+    // weight gradients over the whole tile grid in whole rounds of 256 items:
+    // the blocked item order (a function of the plan alone, so both operand
+    // layouts sum every output in the same order)
+    g.blocked = row_b && tile0 == 0 && ntiles == tiles && p.tiles_m % 4 == 0 && p.tiles_n % 8 == 0 &&
+                (int64_t)ntiles * s % 256 == 0;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     // every tile interior and no ragged K slice: the spread-copy kernels
     const bool interior = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0;
