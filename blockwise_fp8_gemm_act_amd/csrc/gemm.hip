@@ -102,6 +102,7 @@ struct GemmArgs {
   int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
   int bn;          // output tile width: 256, or 192 / 128 for the row-scaled kernel
   int blocked;     // items in XCD blocks of 4 x 8 tiles (tile_of); set by the host
+  int banded;      // tiles in bands of 32 row tiles x all 8 column tiles (tile_of); set by the host
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -407,8 +408,18 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = 
     t.split = item / g.ntiles;
     t.local = item - t.split * g.ntiles;
     const int tile = g.tile0 + t.local;
-    tm = tile % g.tiles_m;               // consecutive items walk down M: they share B
-    tn = tile / g.tiles_m;
+    if (g.banded) {
+      // 8 column tiles, row tiles a multiple of 32, no split, A larger than
+      // the MALL holds: round r is the band of row tiles 32r .. 32r+31, walked
+      // down M through all 8 column tiles, so each XCD's 32 items are 4 row
+      // tiles x 8 column tiles (12 panels, as in the walk below) and each A
+      // panel is read in one round only, instead of once per 4 column tiles
+      tm = ((tile >> 8) << 5) | (tile & 31);
+      tn = (tile >> 5) & 7;
+    } else {
+      tm = tile % g.tiles_m;             // consecutive items walk down M: they share B
+      tn = tile / g.tiles_m;
+    }
     xk = tm & 7;
   }
   t.m0 = tm * kBM;
@@ -1421,6 +1432,13 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     // layouts sum every output in the same order)
     g.blocked = row_b && tile0 == 0 && ntiles == tiles && p.tiles_m % 4 == 0 && p.tiles_n % 8 == 0 &&
                 (int64_t)ntiles * s % 256 == 0;
+    // one unsplit launch over all of 8 column tiles whose A operand is larger
+    // than half the 256 MB MALL (so the walk's second read of each A panel
+    // would come from HBM): row bands, a permutation of the tiles in which
+    // each tile's K order still depends on its row tile alone.  Where A fits
+    // the MALL the walk measured faster.
+    g.banded = !g.blocked && s == 1 && tile0 == 0 && ntiles == tiles && p.tiles_n == 8 && p.tiles_m % 32 == 0 &&
+               M * K > (int64_t(128) << 20);
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     // every tile interior and no ragged K slice: the spread-copy kernels
     const bool interior = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0;

@@ -403,3 +403,21 @@ def test_spread_copy_kernel_matches_edge_kernel(orc, mode, M, N, K):
     ms, ns = (None, None) if M * N <= 1 << 20 else edge_samples(M, N, 20000, seed=M + N)
     check_gemm(orc, mode, np.ascontiguousarray(a[:M]), np.ascontiguousarray(sa[:, :M]), np.ascontiguousarray(b[:N]),
                np.ascontiguousarray(sb[:nb]), inner, "spread mode %d %dx%dx%d" % (mode, M, N, K), ms, ns)
+
+
+@pytest.mark.parametrize("mode", [FPROP, DGRAD])
+def test_row_band_order_matches_walk(orc, mode):
+    """8 column tiles, 32 row tiles and an A operand over 128 MiB: the launch takes its tiles in
+    a row band of 32 row tiles x 8 column tiles.  With 16 more columns (9 column tiles) the
+    same operands run in the plain walk.  Each output's K order depends on its row tile alone,
+    so the shared outputs agree bit for bit (none of them is in a split tile: the 9th column
+    tile holds the only tiles past the first round)."""
+    M, N, K = 8192, 2048, 16512
+    a, sa, b, sb = quantized_operands(orc, mode, M, N + 16, K, seed=97 + mode)
+    nb = N // TILE
+    band = run_gpu(mode, a, sa, np.ascontiguousarray(b[:N]), np.ascontiguousarray(sb[:nb]), torch.bfloat16)
+    walk = run_gpu(mode, a, sa, b, sb, torch.bfloat16)
+    assert np.array_equal(out_np(walk)[:, :N], out_np(band)), "the row band changed the sums"
+    ms, ns = edge_samples(M, N, 20000, seed=M + N + mode)
+    check_gemm(orc, mode, a, sa, np.ascontiguousarray(b[:N]), np.ascontiguousarray(sb[:nb]), band,
+               "row band mode %d %dx%dx%d" % (mode, M, N, K), ms, ns)

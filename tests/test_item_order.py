@@ -10,7 +10,10 @@ writes them and checks, for the layer's weight-gradient plans and a few more:
 - in the blocked order, the 32 items of one XCD and round are one split of a 4 x 8
   group of tiles with one rotation (they walk K in lockstep and share 12 panels);
 - in the row-tile walk with a row-tile count divisible by 8, an XCD's items also share
-  their rotation.
+  their rotation;
+- in the row-band order (one unsplit launch over 8 column tiles whose A operand exceeds
+  128 MiB), each round is a band of 32 row tiles, each XCD's items are 4 x 8 tiles, and
+  every tile keeps the walk's rotation.
 The host sets the blocked order only when the whole grid, times the splits, fills
 rounds of 256 items and the tile counts divide by 4 (rows) and 8 (columns); the
 conditions are checked here as the host code states them.
@@ -22,9 +25,14 @@ def blocked_ok(tiles_m, tiles_n, splits):
     return tiles_m % 4 == 0 and tiles_n % 8 == 0 and (tiles_m * tiles_n * splits) % 256 == 0
 
 
-def tile_of(item, tiles_m, tiles_n, splits, nk, blocked):
+def tile_of(item, tiles_m, tiles_n, splits, nk, blocked, banded=False):
     spl = -(-nk // splits)
-    if blocked:
+    if banded:
+        split, tile = 0, item
+        tm = ((tile >> 8) << 5) | (tile & 31)
+        tn = (tile >> 5) & 7
+        xk = tm & 7
+    elif blocked:
         x = item & 7
         w = (item >> 3) & 31
         blk = ((item >> 8) << 3) | x
@@ -101,3 +109,25 @@ def test_blocked_order_needs_whole_rounds():
     assert not blocked_ok(8, 6, 4)
     assert not blocked_ok(6, 8, 8)
     assert not blocked_ok(4, 8, 1)
+
+
+@pytest.mark.parametrize("tiles_m,nk", [(64, 16), (64, 96), (32, 48), (96, 7)])
+def test_banded_order(tiles_m, nk):
+    """One unsplit launch over 8 column tiles and a multiple of 32 row tiles: bands of 32 row
+    tiles x 8 column tiles, one per round.  Every tile once; each XCD and round holds 4 row
+    tiles x 8 column tiles with one rotation (the row tile's, as in the walk); each row tile's
+    items all run in one round."""
+    items = tiles_m * 8
+    seen, round_of_tm = set(), {}
+    for i in range(items):
+        split, tm, tn, rot, n = tile_of(i, tiles_m, 8, 1, nk, False, banded=True)
+        assert split == 0 and 0 <= tm < tiles_m and 0 <= tn < 8
+        assert rot == tile_of(tn * tiles_m + tm, tiles_m, 8, 1, nk, False)[3], "the walk's rotation"
+        seen.add((tm, tn))
+        assert round_of_tm.setdefault(tm, i // 256) == i // 256
+    assert len(seen) == items
+    for r in range(items // 256):
+        for x in range(8):
+            group = [tile_of(256 * r + 8 * w + x, tiles_m, 8, 1, nk, False, banded=True) for w in range(32)]
+            assert len({g[3] for g in group}) == 1
+            assert len({g[1] for g in group}) == 4 and len({g[2] for g in group}) == 8
