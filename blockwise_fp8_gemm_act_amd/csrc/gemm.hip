@@ -102,7 +102,7 @@ struct GemmArgs {
   int ntiles;      //   (tile t: row tile t % tiles_m, column tile t / tiles_m)
   int bn;          // output tile width: 256, or 192 / 128 for the row-scaled kernel
   int blocked;     // items in XCD blocks of 4 x 8 tiles (tile_of); set by the host
-  int banded;      // tiles in bands of 32 row tiles x all 8 column tiles (tile_of); set by the host
+  int banded;      // tiles numbered in row bands (band_tile); set by the host
   // fused SwiGLU epilogue only: B holds gate rows [0, I) and up rows [I, 2I);
   // out is the optional bf16 gate/up output [M][2I]
   int64_t I;
@@ -373,6 +373,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// Row-band numbering of the tiles of a GEMM with 8 column tiles whose A
+// operand is larger than the MALL holds: tiles 256b .. 256b+255 are band b,
+// row tiles 32b .. 32b+31 (fewer in a last, partial band) across all 8 column
+// tiles, walked down M.  A whole round of 256 items is then one band: each
+// XCD's 32 items are 4 row tiles x 8 column tiles (12 panels, as in the row-tile
+// walk) and each A panel is read in one round only, where the walk reads it
+// once per 4 column tiles.  A plan that computes its first 256 tiles whole and
+// splits the rest splits a band of whole row tiles.
+__host__ __device__ __forceinline__ void band_tile(int tile, int tiles_m, int &tm, int &tn) {
+  const int b = tile >> 8, j = tile & 255;
+  const int h = min(32, tiles_m - 32 * b);
+  tm = 32 * b + j % h;
+  tn = j / h;
+}
+
 // One work item: a 256x256 output tile and one split of its K slices.  All
 // fields are uniform across the workgroup.
 struct Tile {
@@ -409,13 +424,7 @@ __device__ __forceinline__ Tile tile_of(const GemmArgs &g, int item, bool glu = 
     t.local = item - t.split * g.ntiles;
     const int tile = g.tile0 + t.local;
     if (g.banded) {
-      // 8 column tiles, row tiles a multiple of 32, no split, A larger than
-      // the MALL holds: round r is the band of row tiles 32r .. 32r+31, walked
-      // down M through all 8 column tiles, so each XCD's 32 items are 4 row
-      // tiles x 8 column tiles (12 panels, as in the walk below) and each A
-      // panel is read in one round only, instead of once per 4 column tiles
-      tm = ((tile >> 8) << 5) | (tile & 31);
-      tn = (tile >> 5) & 7;
+      band_tile(tile, g.tiles_m, tm, tn);
     } else {
       tm = tile % g.tiles_m;             // consecutive items walk down M: they share B
       tn = tile / g.tiles_m;
@@ -1242,7 +1251,7 @@ __device__ __forceinline__ void reduce_at(const float *ws, void *out, int64_t w,
 template <bool kBf16Out, bool kAcc, bool kVec>
 __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *ws, void *out, int64_t M, int64_t N,
                                                                   int tiles_m, int tile0, int ntiles, int splits,
-                                                                  int bn) {
+                                                                  int bn, int banded) {
   static_assert(!kAcc || !kBf16Out, "accumulate mode is fp32 only");
   constexpr int W = kVec ? 4 : 1;
   const int row_items = bn / W;
@@ -1254,7 +1263,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_tiles_kernel(const float *w
     const int t = (int)(e / (kBM * row_items));
     const int tile = tile0 + t;
     const int r = (int)((e / row_items) % kBM), c = (int)(e % row_items) * W;
-    const int64_t m = (int64_t)(tile % tiles_m) * kBM + r, n = (int64_t)(tile / tiles_m) * bn + c;
+    int tm = tile % tiles_m, tn = tile / tiles_m;
+    if (banded) band_tile(tile, tiles_m, tm, tn);
+    const int64_t m = (int64_t)tm * kBM + r, n = (int64_t)tn * bn + c;
     if (m >= M || n >= N) continue;
     reduce_at<kBf16Out, kAcc, kVec>(ws, out, (int64_t)t * tile_elems + (int64_t)r * bn + c, m * N + n, stride, splits);
   }
@@ -1424,6 +1435,12 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
   g.nk = p.nk; g.tiles_m = p.tiles_m; g.tiles_n = p.tiles_n; g.bn = p.bn;
   const int tiles = p.tiles_m * p.tiles_n;
   const bool row_b = mode == 2 || mode == 3;
+  // 8 column tiles and an A operand larger than half the 256 MB MALL (so the
+  // row-tile walk's second read of each A panel comes from HBM): the tiles
+  // are numbered in row bands (band_tile) by every launch of the GEMM and by
+  // its reduction.  Each tile's K order still depends on its row tile alone.
+  // Where A fits the MALL the walk measured faster.
+  const int banded = p.tiles_n == 8 && p.bn == kBN && M * K > (int64_t(128) << 20);
   // one persistent launch over tiles [tile0, tile0 + ntiles), each split s ways
   auto launch = [&](int tile0, int ntiles, int s, int spl, bool to_ws) {
     g.tile0 = tile0; g.ntiles = ntiles; g.splits = s; g.spl = spl;
@@ -1432,13 +1449,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     // layouts sum every output in the same order)
     g.blocked = row_b && tile0 == 0 && ntiles == tiles && p.tiles_m % 4 == 0 && p.tiles_n % 8 == 0 &&
                 (int64_t)ntiles * s % 256 == 0;
-    // one unsplit launch over all of 8 column tiles whose A operand is larger
-    // than half the 256 MB MALL (so the walk's second read of each A panel
-    // would come from HBM): row bands, a permutation of the tiles in which
-    // each tile's K order still depends on its row tile alone.  Where A fits
-    // the MALL the walk measured faster.
-    g.banded = !g.blocked && s == 1 && tile0 == 0 && ntiles == tiles && p.tiles_n == 8 && p.tiles_m % 32 == 0 &&
-               M * K > (int64_t(128) << 20);
+    g.banded = !g.blocked && banded;
     const dim3 grid((unsigned)std::min<int64_t>((int64_t)ntiles * s, compute_units()));
     // every tile interior and no ragged K slice: the spread-copy kernels
     const bool interior = p.bn == kBN && M % kBM == 0 && N % kBN == 0 && K % kBK == 0;
@@ -1483,7 +1494,7 @@ hipError_t run_gemm(int mode, const uint8_t *a, const float *sa, const uint8_t *
     const int64_t n = (int64_t)nt * kBM * p.bn / W;
     const int blocks = (int)std::min<int64_t>((n + 255) / 256, 8192);
     hipLaunchKernelGGL((splitk_reduce_tiles_kernel<kB, kA, kV>), dim3(blocks), dim3(256), 0, stream, w, out, M, N,
-                       p.tiles_m, p.whole, nt, p.splits, p.bn);
+                       p.tiles_m, p.whole, nt, p.splits, p.bn, g.banded);   // the split launch's numbering
   };
   using T = std::true_type;
   using F = std::false_type;

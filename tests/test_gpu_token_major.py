@@ -81,10 +81,12 @@ def test_integer_valued_bit_exact(orc, M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 2048), (400, 272, 1040), (2048, 2048, 16384), (4096, 2048, 16384),
                                    (2048, 6144, 8192), (16, 16, 16), (2048, 6144, 1024), (2000, 6096, 1040),
-                                   (4096, 2048, 2048), (2000, 1984, 8000)])
+                                   (4096, 2048, 2048), (2000, 1984, 8000), (9216, 2048, 16384)])
 def test_equals_wgrad_on_transposed_operands(M, N, K):
-    """Same products, same promotion order: the bits of PURO_WGRAD on a^T, b^T.  The last four
-    shapes plan 192- or 128-column tiles (whole and ragged), which both layouts then use."""
+    """Same products, same promotion order: the bits of PURO_WGRAD on a^T, b^T.  (2048, 6144, 1024)
+    to (2000, 1984, 8000) plan 192- or 128-column tiles (whole and ragged), which both layouts
+    then use.  (9216, 2048, 16384) numbers its 288 tiles in row bands (A over 128 MiB) and
+    computes 256 of them whole and the other 32 split over K."""
     a, sa, b, sb = operands(M, N, K, M + 7 * N + K)
     for dtype in (torch.float32, torch.bfloat16):
         got = run(WGRAD_TM, a, sa, b, sb, dtype)

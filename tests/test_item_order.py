@@ -25,12 +25,19 @@ def blocked_ok(tiles_m, tiles_n, splits):
     return tiles_m % 4 == 0 and tiles_n % 8 == 0 and (tiles_m * tiles_n * splits) % 256 == 0
 
 
-def tile_of(item, tiles_m, tiles_n, splits, nk, blocked, banded=False):
+def band_tile(tile, tiles_m):
+    b, j = tile >> 8, tile & 255
+    h = min(32, tiles_m - 32 * b)
+    return 32 * b + j % h, j // h
+
+
+def tile_of(item, tiles_m, tiles_n, splits, nk, blocked, banded=False, tile0=0, ntiles=None):
     spl = -(-nk // splits)
+    if ntiles is None:
+        ntiles = tiles_m * tiles_n
     if banded:
-        split, tile = 0, item
-        tm = ((tile >> 8) << 5) | (tile & 31)
-        tn = (tile >> 5) & 7
+        split = item // ntiles
+        tm, tn = band_tile(tile0 + item - split * ntiles, tiles_m)
         xk = tm & 7
     elif blocked:
         x = item & 7
@@ -111,7 +118,7 @@ def test_blocked_order_needs_whole_rounds():
     assert not blocked_ok(4, 8, 1)
 
 
-@pytest.mark.parametrize("tiles_m,nk", [(64, 16), (64, 96), (32, 48), (96, 7)])
+@pytest.mark.parametrize("tiles_m,nk", [(64, 16), (64, 96), (32, 48), (96, 7), (48, 128), (16, 300), (45, 20)])
 def test_banded_order(tiles_m, nk):
     """One unsplit launch over 8 column tiles and a multiple of 32 row tiles: bands of 32 row
     tiles x 8 column tiles, one per round.  Every tile once; each XCD and round holds 4 row
@@ -127,7 +134,31 @@ def test_banded_order(tiles_m, nk):
         assert round_of_tm.setdefault(tm, i // 256) == i // 256
     assert len(seen) == items
     for r in range(items // 256):
+        if tiles_m - 32 * r < 32:
+            break
         for x in range(8):
             group = [tile_of(256 * r + 8 * w + x, tiles_m, 8, 1, nk, False, banded=True) for w in range(32)]
             assert len({g[3] for g in group}) == 1
             assert len({g[1] for g in group}) == 4 and len({g[2] for g in group}) == 8
+
+
+@pytest.mark.parametrize("tiles_m,whole,splits,nk", [(48, 256, 2, 128), (40, 256, 3, 64), (96, 512, 2, 40)])
+def test_banded_whole_then_split(tiles_m, whole, splits, nk):
+    """A plan that computes its first tiles whole and splits the rest: in the row-band
+    numbering the two launches cover every tile once, the split launch's tiles are whole row
+    tiles (every column tile of each), and all of a tile's splits cover its K range once."""
+    tiles = tiles_m * 8
+    cover = {}
+    for i in range(whole):
+        _, tm, tn, _, n = tile_of(i, tiles_m, 8, 1, nk, False, banded=True, tile0=0, ntiles=whole)
+        cover.setdefault((tm, tn), []).append((0, n))
+    split_rows = set()
+    for i in range((tiles - whole) * splits):
+        split, tm, tn, _, n = tile_of(i, tiles_m, 8, splits, nk, False, banded=True, tile0=whole,
+                                      ntiles=tiles - whole)
+        cover.setdefault((tm, tn), []).append((split, n))
+        split_rows.add(tm)
+    assert len(cover) == tiles
+    for (tm, tn), parts in cover.items():
+        assert sum(n for _, n in parts) == nk and len({s for s, _ in parts}) == len(parts)
+    assert all(len(cover[(tm, tn)]) == splits for tm in split_rows for tn in range(8))
