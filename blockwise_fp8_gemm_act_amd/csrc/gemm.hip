@@ -785,8 +785,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_bw_kernel(GemmArgs g) {
     auto promote = [&](int pb, int mb) {
       const v4f prev = kFirst ? (v4f){0.f, 0.f, 0.f, 0.f} : acc[mb][pb];
       if constexpr (kRowScaledB) {
-        const v4f ps = P[mb] * sbv[pb];                          // column scale first, in place
-        acc[mb][pb] = __builtin_elementwise_fma(ps, (v4f)sa[mb], prev);
+        // the scale products sA * sB need no MFMA result: only the FMA waits for P
+        acc[mb][pb] = __builtin_elementwise_fma(P[mb], sbv[pb] * (v4f)sa[mb], prev);
       } else {
         acc[mb][pb] = __builtin_elementwise_fma(P[mb], (v4f)((kGlu && (pb & 1)) ? scu[mb] : sc[mb]), prev);
       }
