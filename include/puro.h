@@ -248,7 +248,12 @@ size_t puro_gemm_workspace_bytes(puro_gemm_mode mode, int64_t M, int64_t N, int6
  *        entry do not matter.
  * K must be a multiple of 16; M and N are free.  Each 128-deep slice of K is
  * accumulated by the matrix cores in fp32 and promoted into the fp32
- * accumulator with its scales; the result is deterministic for a given shape.
+ * accumulator with its scales, acc += P * fp32(sA * sB); the result is
+ * deterministic for a given shape.  Domain: every product sA * sB that a slice
+ * uses must be a normal fp32 value (2^-126 .. 2^128).  Outside it the product
+ * underflows or overflows (not detected); scales from the quantizers leave it
+ * only when the product of the two tiles' maxima is below ~2^-108 (both below
+ * ~2^-54) or above ~2^145.
  */
 puro_status puro_gemm_fp8_blockwise(puro_gemm_mode mode,
                                     const uint8_t *a, const float *sa,
